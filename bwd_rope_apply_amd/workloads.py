@@ -1,0 +1,164 @@
+"""Seeded synthetic workloads for exact causal RoPE attention.
+
+This module draws inputs and nothing else: it holds none of the attention or
+rotation arithmetic, so both the HIP path and the float64 oracle can take their
+inputs from it without sharing any of the method.
+
+Recipe (same for every workload):
+  * a numpy PCG64 generator per tensor, seeded from
+    ``SeedSequence(seed).spawn(5)`` and used in the fixed order
+    [Q, K, V, dO, alpha];
+  * draws are float64, then rounded to the storage type with
+    round-to-nearest-even (float64 -> float32, and float32 -> bfloat16 for
+    bf16 storage);
+  * Q, K, V, dO are contiguous [B, H, N, D], D fastest; alpha is one [D/2]
+    float32 vector shared by every batch and head.
+
+The five named workloads follow the settings of the pages: one attention
+layer at the LeRoPE training length 2048 with head dim 128, a training-step
+shape, a long-context shape with bounded entries (the bounded-entries regime
+of "RoPE attention can be trained in almost-linear time", Problem definition)
+and learned-spectrum-like alpha (LeRoPE, "Main results" on the dominant band
+and suppressed slow bands), and a very long context at head dim 64 (LeRoPE,
+"Experimental setup").  No dataset is used; the i.i.d. tensors stand in for
+activations of those shapes.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# (kind, a, b): "uniform" U[a,b]; "normal" N(0, a^2) scaled by b; "zero".
+Dist = Tuple[str, float, float]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str          # storage type of Q, K, V, dO: "fp32" or "bf16"
+    base: float
+    causal: bool
+    qk: Dist
+    v: Dist
+    do: Dist
+    alpha: Dist
+    seed: int
+    note: str = ""
+
+    def with_shape(self, B=None, H=None, N=None, seed=None) -> "Workload":
+        """Same distributions at another shape (parity cases at reduced size)."""
+        return dataclasses.replace(
+            self, B=B or self.B, H=H or self.H, N=N or self.N,
+            seed=self.seed if seed is None else seed,
+            name=f"{self.name}[B{B or self.B},H{H or self.H},N{N or self.N}]")
+
+    @property
+    def n_elem(self) -> int:
+        return self.B * self.H * self.N * self.D
+
+
+_INV_SQRT_128 = 1.0 / np.sqrt(128.0)
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_fp32": Workload(
+        "tiny_fp32", 1, 1, 128, 64, "fp32", 1e4, True,
+        qk=("uniform", -1.0, 1.0), v=("uniform", -1.0, 1.0),
+        do=("uniform", -1.0, 1.0), alpha=("zero", 0.0, 0.0), seed=1000,
+        note="tiny exact check, standard RoPE (alpha = 0)"),
+    "layer_2k": Workload(
+        "layer_2k", 1, 16, 2048, 128, "bf16", 1e4, True,
+        qk=("normal", 1.0, 1.0), v=("normal", 1.0, 1.0),
+        do=("normal", 1.0, 1.0), alpha=("normal", 0.1, 1.0), seed=1001,
+        note="single layer at training length 2048"),
+    "train_4k": Workload(
+        "train_4k", 4, 32, 4096, 128, "bf16", 5e5, True,
+        qk=("normal", 1.0, _INV_SQRT_128), v=("normal", 1.0, 1.0),
+        do=("normal", 1.0, 1.0), alpha=("zero", 0.0, 0.0), seed=1002,
+        note="training-step shape, near-uniform attention"),
+    "long_8k": Workload(
+        "long_8k", 1, 32, 8192, 128, "bf16", 1e4, True,
+        qk=("uniform", -2.0, 2.0), v=("uniform", -2.0, 2.0),
+        do=("normal", 1.0, 1.0), alpha=("uniform", -1.0, 0.5), seed=1003,
+        note="long-context headline, bounded entries, learned-like alpha"),
+    "vlong_32k": Workload(
+        "vlong_32k", 1, 8, 32768, 64, "bf16", 1e6, True,
+        qk=("normal", 1.0, 1.0), v=("normal", 1.0, 1.0),
+        do=("normal", 1.0, 1.0), alpha=("normal", 0.2, 1.0), seed=1004,
+        note="very long context, head dim 64"),
+}
+
+HEADLINE = "long_8k"
+
+
+def _draw(rng: np.random.Generator, dist: Dist, shape) -> np.ndarray:
+    kind, a, b = dist
+    if kind == "uniform":
+        return rng.uniform(a, b, size=shape)
+    if kind == "normal":
+        return rng.normal(0.0, a, size=shape) * b
+    if kind == "zero":
+        return np.zeros(shape)
+    raise ValueError(kind)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bfloat16 bit patterns to float64."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Stored inputs.  ``q, k, v, do`` hold the storage bits (float32 arrays,
+    or uint16 bfloat16 bit patterns); ``alpha`` is float32 [D/2]."""
+    wl: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    alpha: np.ndarray
+
+    def f64(self, name: str) -> np.ndarray:
+        x = getattr(self, name)
+        if x.dtype == np.uint16:
+            return bf16_bits_to_f64(x)
+        return x.astype(np.float64)
+
+
+def make_inputs(wl: Workload, which=("q", "k", "v", "do")) -> Inputs:
+    """Draw the stored inputs of ``wl``.  Streams are spawned in the fixed
+    order [Q, K, V, dO, alpha]; tensors not in ``which`` are not drawn (their
+    stream is still consumed by nobody, so the others do not change)."""
+    shape = (wl.B, wl.H, wl.N, wl.D)
+    streams = np.random.SeedSequence(wl.seed).spawn(5)
+    dists = {"q": wl.qk, "k": wl.qk, "v": wl.v, "do": wl.do}
+    out = {}
+    for idx, name in enumerate(("q", "k", "v", "do")):
+        if name not in which:
+            out[name] = None
+            continue
+        x = _draw(np.random.Generator(np.random.PCG64(streams[idx])), dists[name], shape)
+        x32 = x.astype(np.float32)
+        out[name] = f32_to_bf16_bits(x32) if wl.dtype == "bf16" else x32
+    a = _draw(np.random.Generator(np.random.PCG64(streams[4])), wl.alpha, (wl.D // 2,))
+    return Inputs(wl, out["q"], out["k"], out["v"], out["do"], a.astype(np.float32))
+
+
+def get(name: str, B: Optional[int] = None, H: Optional[int] = None,
+        N: Optional[int] = None, seed: Optional[int] = None) -> Workload:
+    wl = WORKLOADS[name]
+    if B is None and H is None and N is None and seed is None:
+        return wl
+    return wl.with_shape(B, H, N, seed)
