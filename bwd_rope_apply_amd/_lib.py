@@ -1,0 +1,159 @@
+"""ctypes binding of librope_attn.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers, allocates outputs and the
+workspace with torch on the inputs' device, and passes torch's current HIP
+stream.  There is no fallback: if the library is missing, importing the
+functions below raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librope_attn.so")
+
+FP32, BF16 = 0, 1
+STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
+          -5: "ERR_WORKSPACE", -6: "ERR_HIP", -7: "ERR_ARG"}
+
+_lib = None
+
+
+class RopeAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: status {status} ({STATUS.get(status, '?')}): {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not found: build it with `python -m bwd_rope_apply_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i, d = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_double
+    lib.rope_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.rope_attn_fwd_workspace_bytes.restype = sz
+    lib.rope_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.rope_attn_bwd_workspace_bytes.restype = sz
+    lib.rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, vp, i, vp, sz, vp]
+    lib.rope_attn_fwd.restype = i
+    lib.rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, vp, i,
+                                  vp, sz, vp]
+    lib.rope_attn_bwd.restype = i
+    lib.rope_attn_status_string.argtypes = [i]
+    lib.rope_attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise RopeAttnError(fn, status, load().rope_attn_status_string(status).decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"q/k/v/dO must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _shape(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    return tuple(int(x) for x in q.shape)
+
+
+def _alpha(alpha, q, D):
+    import torch
+    if alpha is None:
+        return None
+    if alpha.shape != (D // 2,) or alpha.dtype != torch.float32 or alpha.device != q.device:
+        raise ValueError("alpha must be a float32 [D/2] tensor on q's device")
+    return alpha.contiguous()
+
+
+def workspace_bytes(kind: str, B: int, H: int, N: int, D: int, dtype: int, causal: bool) -> int:
+    lib = load()
+    f = lib.rope_attn_fwd_workspace_bytes if kind == "fwd" else lib.rope_attn_bwd_workspace_bytes
+    return int(f(B, H, N, D, dtype, int(causal)))
+
+
+def fwd(q, k, v, base: float, alpha=None, causal: bool = True, workspace=None,
+        out: Optional[Tuple] = None):
+    """O [B,H,N,D] float32 and LSE [B,H,N] float32 for rotated attention."""
+    import torch
+    lib = load()
+    B, H, N, D = _shape(q, k, v)
+    dt = _dtype_code(q)
+    alpha = _alpha(alpha, q, D)
+    if out is None:
+        o = torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    nbytes = workspace_bytes("fwd", B, H, N, D, dt, causal)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.rope_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D, dt,
+                           float(base), _ptr(alpha), int(causal), _ptr(workspace),
+                           workspace.numel(), _stream(q.device))
+    _check("rope_attn_fwd", st)
+    return o, lse
+
+
+def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, workspace=None,
+        want_dalpha: bool = True, out: Optional[Tuple] = None):
+    """(dQ, dK, dV [B,H,N,D] float32, dalpha [D/2] float32 or None)."""
+    import torch
+    lib = load()
+    B, H, N, D = _shape(q, k, v)
+    dt = _dtype_code(q)
+    if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous():
+        raise ValueError("dO must match q in shape and dtype and be contiguous")
+    if o.shape != q.shape or o.dtype != torch.float32 or not o.is_contiguous():
+        raise ValueError("O must be a contiguous float32 [B,H,N,D] tensor")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("LSE must be a contiguous float32 [B,H,N] tensor")
+    alpha = _alpha(alpha, q, D)
+    if out is None:
+        dq = torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+        dk = torch.empty_like(dq)
+        dv = torch.empty_like(dq)
+        da = torch.empty((D // 2,), dtype=torch.float32, device=q.device) if want_dalpha else None
+    else:
+        dq, dk, dv, da = out
+    nbytes = workspace_bytes("bwd", B, H, N, D, dt, causal)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.rope_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(da), B, H, N, D, dt, float(base),
+                           _ptr(alpha), int(causal), _ptr(workspace), workspace.numel(),
+                           _stream(q.device))
+    _check("rope_attn_bwd", st)
+    return dq, dk, dv, da

@@ -1,0 +1,262 @@
+// C ABI: argument validation, workspace layout and the launch sequence of
+// the forward and backward passes.
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "rope_attn.h"
+
+namespace {
+
+using namespace ra;
+
+constexpr size_t ALIGN = 256;
+
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Shape {
+  int B, H, N, D, dtype, causal;
+  size_t bh() const { return (size_t)B * H; }
+  size_t elems() const { return bh() * N * D; }
+  bool bf16() const { return dtype == ROPE_ATTN_BF16; }
+  // exact-corner rows: bf16 causal only
+  int corner() const { return (bf16() && causal) ? CORNER : 0; }
+};
+
+int check_shape(const Shape& s) {
+  if (s.dtype != ROPE_ATTN_FP32 && s.dtype != ROPE_ATTN_BF16) return ROPE_ATTN_ERR_DTYPE;
+  if (s.B < 1 || s.H < 1 || s.N < 1) return ROPE_ATTN_ERR_SHAPE;
+  if (s.D != 64 && s.D != 128) return ROPE_ATTN_ERR_SHAPE;
+  if (s.causal != 0 && s.causal != 1) return ROPE_ATTN_ERR_ARG;
+  // keep every index of the kernels inside int / 2^40-element ranges
+  if (s.N > (1 << 24) || s.bh() > (1u << 24) || s.elems() > ((size_t)1 << 40)) return ROPE_ATTN_ERR_SHAPE;
+  if ((size_t)s.N * (s.D / 2) > (size_t)INT32_MAX) return ROPE_ATTN_ERR_SHAPE;
+  return ROPE_ATTN_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+// Workspace regions, in order.  Sizes are 0 for regions a call does not use.
+struct Layout {
+  size_t theta, cs, qh, kh, vh, doh, drow, dkp, dvp, part;
+  int slots;
+  size_t total() const { return theta + cs + qh + kh + vh + doh + drow + dkp + dvp + part; }
+};
+
+MfmaParams mfma_base(const Shape& s) {
+  MfmaParams m = {};
+  m.B = s.B; m.H = s.H; m.N = s.N; m.D = s.D;
+  m.corner = s.corner();
+  m.causal = s.causal;
+  m.bf16 = s.bf16();
+  m.scale = 1.0f / sqrtf((float)s.D);
+  return m;
+}
+
+Layout layout(const Shape& s, bool bwd) {
+  Layout L = {};
+  L.theta = up(sizeof(double) * (s.D / 2));
+  L.cs = up(sizeof(float2) * (size_t)s.N * (s.D / 2));
+  const size_t h16 = up(2 * s.elems());
+  if (s.bf16()) {
+    L.qh = L.kh = L.vh = h16;
+    if (bwd) L.doh = h16;
+  }
+  if (bwd) {
+    L.drow = up(sizeof(float) * s.bh() * s.N);
+    if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * CORNER * s.D);
+    if (s.bf16()) {
+      const MfmaParams m = mfma_base(s);
+      L.slots = (s.corner() ? simt_slots((int)s.bh(), CORNER) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
+    } else {
+      L.slots = 2 * simt_slots((int)s.bh(), s.N);
+    }
+    L.part = up(sizeof(float) * (size_t)L.slots * (s.D / 2));
+  }
+  return L;
+}
+
+struct Carve {
+  char* p;
+  template <class T>
+  T* take(size_t bytes) {
+    if (!bytes) return nullptr;
+    T* r = reinterpret_cast<T*>(p);
+    p += bytes;
+    return r;
+  }
+};
+
+int check_common(const Shape& s, double base, void* ws, size_t ws_bytes, bool bwd) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!(base > 0.0) || !isfinite(base)) return ROPE_ATTN_ERR_ARG;
+  if (!ws) return ROPE_ATTN_ERR_NULL;
+  if (misaligned(ws)) return ROPE_ATTN_ERR_ALIGN;
+  if (ws_bytes < layout(s, bwd).total()) return ROPE_ATTN_ERR_WORKSPACE;
+  return ROPE_ATTN_OK;
+}
+
+void tables(const Shape& s, double base, const float* alpha, double* theta, float2* cs,
+            hipStream_t st) {
+  TableParams t = {};
+  t.cs = cs; t.theta_hat = theta; t.alpha = alpha; t.base = base; t.N = s.N; t.D = s.D;
+  launch_table(t, st);
+}
+
+int finish() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? ROPE_ATTN_OK : ROPE_ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rope_attn_fwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal) {
+  const Shape s{B, H, N, D, dtype, causal};
+  if (check_shape(s)) return 0;
+  return layout(s, false).total();
+}
+
+size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal) {
+  const Shape s{B, H, N, D, dtype, causal};
+  if (check_shape(s)) return 0;
+  return layout(s, true).total();
+}
+
+int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+                  int N, int D, int dtype, double base, const float* alpha, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const Shape s{B, H, N, D, dtype, causal};
+  if (!q || !k || !v || !o || !lse) return ROPE_ATTN_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
+      misaligned(alpha))
+    return ROPE_ATTN_ERR_ALIGN;
+  int st = check_common(s, base, workspace, workspace_bytes, false);
+  if (st) return st;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const Layout L = layout(s, false);
+  Carve c{reinterpret_cast<char*>(workspace)};
+  double* theta = c.take<double>(L.theta);
+  float2* cs = c.take<float2>(L.cs);
+  half_t* qh = c.take<half_t>(L.qh);
+  half_t* kh = c.take<half_t>(L.kh);
+  half_t* vh = c.take<half_t>(L.vh);
+  tables(s, base, alpha, theta, cs, hs);
+
+  SimtParams sp = {};
+  sp.q = q; sp.k = k; sp.v = v; sp.cs = cs; sp.out_o = o; sp.out_lse = lse;
+  sp.bf16 = s.bf16(); sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
+  sp.scale = 1.0f / sqrtf((float)D);
+  if (!s.bf16()) {
+    sp.rows = N;
+    launch_simt_fwd(sp, hs);
+    return finish();
+  }
+  PrepParams pp = {};
+  pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
+  pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
+  launch_prep(pp, hs);
+  if (s.corner()) {
+    sp.rows = CORNER;
+    launch_simt_fwd(sp, hs);
+  }
+  MfmaParams mp = mfma_base(s);
+  mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.o = o; mp.out_lse = lse;
+  launch_fwd_mfma(mp, hs);
+  return finish();
+}
+
+int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, const void* dO,
+                  const float* lse, float* dq, float* dk, float* dv, float* dalpha, int B, int H,
+                  int N, int D, int dtype, double base, const float* alpha, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const Shape s{B, H, N, D, dtype, causal};
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ROPE_ATTN_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dO) ||
+      misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(alpha) ||
+      misaligned(dalpha))
+    return ROPE_ATTN_ERR_ALIGN;
+  int st = check_common(s, base, workspace, workspace_bytes, true);
+  if (st) return st;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const Layout L = layout(s, true);
+  Carve c{reinterpret_cast<char*>(workspace)};
+  double* theta = c.take<double>(L.theta);
+  float2* cs = c.take<float2>(L.cs);
+  half_t* qh = c.take<half_t>(L.qh);
+  half_t* kh = c.take<half_t>(L.kh);
+  half_t* vh = c.take<half_t>(L.vh);
+  half_t* doh = c.take<half_t>(L.doh);
+  float* drow = c.take<float>(L.drow);
+  float* dkp = c.take<float>(L.dkp);
+  float* dvp = c.take<float>(L.dvp);
+  float* part = c.take<float>(L.part);
+  tables(s, base, alpha, theta, cs, hs);
+
+  PrepParams pp = {};
+  pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
+  pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
+  pp.bf16 = s.bf16(); pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
+  launch_prep(pp, hs);
+
+  SimtParams sp = {};
+  sp.q = q; sp.k = k; sp.v = v; sp.dO = dO; sp.o = o; sp.lse = lse; sp.drow = drow; sp.cs = cs;
+  sp.dq = dq; sp.dk = dk; sp.dv = dv; sp.dk_part = dkp; sp.dv_part = dvp;
+  sp.dalpha_part = part;
+  sp.bf16 = s.bf16(); sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
+  sp.scale = 1.0f / sqrtf((float)D);
+  int slot = 0;
+  if (!s.bf16()) {
+    sp.rows = N; sp.qend = N; sp.final_ = 1;
+    sp.slot0 = slot;
+    launch_simt_dq(sp, hs);
+    slot += simt_slots((int)s.bh(), N);
+    sp.slot0 = slot;
+    launch_simt_dkdv(sp, hs);
+    slot += simt_slots((int)s.bh(), N);
+  } else {
+    if (s.corner()) {
+      sp.rows = CORNER; sp.qend = N < CORNER ? N : CORNER; sp.final_ = 0;
+      sp.slot0 = slot;
+      launch_simt_dq(sp, hs);
+      slot += simt_slots((int)s.bh(), CORNER);
+      launch_simt_dkdv(sp, hs);  // rotated-frame partials, no d alpha slots
+    }
+    MfmaParams mp = mfma_base(s);
+    mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.q = q; mp.k = k; mp.cs = cs;
+    mp.lse = lse; mp.drow = drow; mp.dq = dq; mp.dk = dk; mp.dv = dv;
+    mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
+    mp.slot0 = slot;
+    launch_dq_mfma(mp, hs);
+    slot += dq_mfma_slots(mp);
+    mp.slot0 = slot;
+    launch_dkdv_mfma(mp, hs);
+    slot += dkdv_mfma_slots(mp);
+  }
+  if (dalpha) {
+    DalphaParams dp = {};
+    dp.part = part; dp.theta_hat = theta; dp.dalpha = dalpha; dp.slots = slot; dp.D = D;
+    launch_dalpha_reduce(dp, hs);
+  }
+  return finish();
+}
+
+const char* rope_attn_status_string(int status) {
+  switch (status) {
+    case ROPE_ATTN_OK: return "ok";
+    case ROPE_ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ROPE_ATTN_ERR_SHAPE: return "invalid shape: need B, H, N >= 1 and D in {64, 128}";
+    case ROPE_ATTN_ERR_DTYPE: return "dtype must be ROPE_ATTN_FP32 or ROPE_ATTN_BF16";
+    case ROPE_ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case ROPE_ATTN_ERR_WORKSPACE: return "workspace smaller than the *_workspace_bytes query";
+    case ROPE_ATTN_ERR_HIP: return "HIP runtime reported a launch error";
+    case ROPE_ATTN_ERR_ARG: return "base must be finite and > 0, causal must be 0 or 1";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Shared device helpers and launch parameter blocks for the RoPE attention
+// kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef _Float16 half_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 half8;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2v;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// Query rows [0, CORNER) of every head (and the keys they see under the
+// causal mask) are computed by the exact fp32 path when the inputs are
+// bf16: those rows average few keys, so their outputs and gradients are the
+// largest entries of each tensor and fp16 operand rounding there would
+// dominate the error relative to the tensor's RMS.
+constexpr int CORNER = 128;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ params
+struct TableParams {
+  float2* cs;           // [N][D/2] (cos, sin) of p * theta_hat_m
+  double* theta_hat;    // [D/2]
+  const float* alpha;   // [D/2] or null (all zero)
+  double base;
+  int N, D;
+};
+
+struct PrepParams {
+  const void* q; const void* k; const void* v; const void* dO;  // [B,H,N,D] inputs
+  const float* o;        // [B,H,N,D] forward output (for D = rowsum(dO*O)), or null
+  const float2* cs;      // [N][D/2]
+  half_t* qh; half_t* kh; half_t* vh; half_t* doh;  // fp16 operand planes, any may be null
+  float* drow;           // [B,H,N] or null
+  int bf16;              // input storage: 1 = bf16, 0 = fp32
+  int BH, N, D;
+};
+
+// Exact fp32 path (one query or key row per 4-lane group).
+struct SimtParams {
+  const void* q; const void* k; const void* v; const void* dO;
+  const float* o; const float* lse; const float* drow;
+  const float2* cs;
+  float* out_o; float* out_lse;        // forward outputs
+  float* dq;                            // [B,H,N,D] un-rotated dQ
+  float* dk; float* dv;                 // final dK, dV (when final != 0)
+  float* dk_part; float* dv_part;       // [BH][rows][D] rotated-frame partials (final == 0)
+  float* dalpha_part;                   // [slots][D/2]
+  int slot0;                            // first dalpha slot of this launch
+  int bf16;
+  int BH, N, D;
+  int rows;        // query rows (fwd, dq) or key rows (dkdv) handled: [0, rows)
+  int qend;        // dkdv: contributions from query rows [.., qend)
+  int causal;
+  int final_;      // dkdv: 1 = write dK/dV, 0 = write rotated partials
+  float scale;
+};
+
+struct MfmaParams {
+  const half_t* qh; const half_t* kh; const half_t* vh; const half_t* doh;
+  const void* q; const void* k;        // original inputs (for the d alpha wedge)
+  const float2* cs;
+  const float* lse; const float* drow;
+  float* o; float* out_lse;
+  float* dq; float* dk; float* dv;
+  const float* dk_part; const float* dv_part;   // corner partials [BH][corner][D] or null
+  float* dalpha_part;
+  int slot0;
+  int bf16;
+  int B, H, N, D;
+  int corner;      // rows [0, corner) are done by the exact path
+  int causal;
+  float scale;
+};
+
+struct DalphaParams {
+  const float* part;     // [slots][D/2]
+  const double* theta_hat;
+  float* dalpha;         // [D/2]
+  int slots, D;
+};
+
+// ------------------------------------------------------------------ launchers
+void launch_table(const TableParams& p, hipStream_t s);
+void launch_prep(const PrepParams& p, hipStream_t s);
+void launch_simt_fwd(const SimtParams& p, hipStream_t s);
+void launch_simt_dq(const SimtParams& p, hipStream_t s);
+void launch_simt_dkdv(const SimtParams& p, hipStream_t s);
+int simt_slots(int BH, int rows);       // dalpha slots used by one simt dq/dkdv launch
+void launch_fwd_mfma(const MfmaParams& p, hipStream_t s);
+void launch_dq_mfma(const MfmaParams& p, hipStream_t s);
+void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);
+int dq_mfma_slots(const MfmaParams& p);
+int dkdv_mfma_slots(const MfmaParams& p);
+void launch_dalpha_reduce(const DalphaParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Load 4 consecutive input elements (bf16 or fp32 storage) as floats.
+__device__ __forceinline__ void load4(const void* base, size_t idx, int bf16, float* x) {
+  if (bf16) {
+    uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else {
+    float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+  }
+}
+
+// Turn the pair (x0, x1) by +phi given (cos phi, sin phi).
+__device__ __forceinline__ void rot(float c, float s, float& x0, float& x1) {
+  float a = x0 * c - x1 * s;
+  float b = x0 * s + x1 * c;
+  x0 = a; x1 = b;
+}
+// Turn the pair by -phi (transpose rotation, the chain rule of rot).
+__device__ __forceinline__ void unrot(float c, float s, float& g0, float& g1) {
+  float a = g0 * c + g1 * s;
+  float b = -g0 * s + g1 * c;
+  g0 = a; g1 = b;
+}
+
+}  // namespace ra

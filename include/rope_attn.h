@@ -1,0 +1,106 @@
+/*
+ * rope_attn.h -- exact softmax attention with rotary position embedding and
+ * learnable per-band log-frequencies, forward and backward, on AMD gfx950.
+ *
+ * What is computed (all four entry points share these conventions):
+ *
+ *   theta_m     = base^(-2m/D),  theta_hat_m = exp(alpha_m) * theta_m,
+ *                 m = 0 .. D/2-1  (LeRoPE, "Central mechanism"; alpha = 0 is
+ *                 standard RoPE, "Key design choices", initialisation)
+ *   rotation    the pair (x[2m], x[2m+1]) of query and key row p is turned
+ *               counter-clockwise by p * theta_hat_m (LeRoPE, "Problem
+ *               statement": queries and keys are rotated in 2-D frequency
+ *               bands; values are not rotated), positions p = 0 .. N-1
+ *   scores      S = Q~ K~^T / sqrt(D), causal mask keeps key j <= query i
+ *   forward     O = softmax(S) V, LSE_i = log sum_j exp(S_ij)   (natural log)
+ *               ("RoPE attention can be trained in almost-linear time",
+ *               "Problem definition"; s(x) in "Methodology", item 1)
+ *   backward    the vector-Jacobian product for the upstream gradient dO:
+ *               beta = dO V^T, dS = P o (beta - D_i) with D_i = sum_c dO O,
+ *               i.e. gamma = diag(s) beta - s s^T beta (same page,
+ *               "Methodology", items 1 and 2, gamma_1 and gamma_2), returned
+ *               as dQ, dK (un-rotated frame), dV, and
+ *   d alpha     dalpha_m = theta_hat_m * sum over batch, heads and positions
+ *               p of p * (x[2m] g[2m+1] - x[2m+1] g[2m]) for (x, g) = (q, dQ)
+ *               and (k, dK): one alpha vector is shared by every head and
+ *               layer (LeRoPE, "Key design choices", parameter sharing), so
+ *               its gradient sums over all of them.  It equals theta_hat_m
+ *               times the slope of the surrogate of LeRoPE, "Theoretical
+ *               analysis".
+ *
+ * Layout: Q, K, V, dO, O, dQ, dK, dV are contiguous [B][H][N][D] with D
+ * fastest; LSE is [B][H][N]; alpha and dalpha are [D/2] float32 shared by all
+ * (b, h).  Q, K, V, dO are stored as float32 (dtype ROPE_ATTN_FP32) or
+ * bfloat16 (ROPE_ATTN_BF16); every output is float32.
+ *
+ * Pointers: all tensor pointers are device pointers (hipMalloc'd or
+ * equivalent), 16-byte aligned.  The caller owns every buffer; the library
+ * allocates nothing and keeps no state between calls.  `stream` is a
+ * hipStream_t (NULL = the default stream); all work is enqueued on it
+ * asynchronously and nothing is synchronised on the host.  Inputs are read
+ * only.  Outputs are overwritten, dalpha included (not accumulated).
+ *
+ * Errors: every entry point validates its arguments before launching
+ * anything and returns ROPE_ATTN_OK or a negative status; no exception or
+ * abort crosses this boundary.  A launch failure reported by the HIP runtime
+ * returns ROPE_ATTN_ERR_HIP.
+ *
+ * Numerics: with bf16 inputs, products run on fp16 matrix-core operands with
+ * float32 accumulation, except the leading causal corner (query rows < 128)
+ * which, like every call with fp32 inputs, runs in float32 throughout.  The
+ * fp16 operands require |Q|, |K|, |V|, |dO| entries below 6.5e4.
+ */
+#ifndef ROPE_ATTN_H
+#define ROPE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ROPE_ATTN_FP32 = 0, ROPE_ATTN_BF16 = 1 } rope_attn_dtype;
+
+typedef enum {
+  ROPE_ATTN_OK = 0,
+  ROPE_ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+  ROPE_ATTN_ERR_SHAPE = -2,     /* B, H, N < 1, D not 64 or 128, or sizes overflow */
+  ROPE_ATTN_ERR_DTYPE = -3,     /* dtype not a rope_attn_dtype */
+  ROPE_ATTN_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+  ROPE_ATTN_ERR_WORKSPACE = -5, /* workspace smaller than the *_workspace_bytes query */
+  ROPE_ATTN_ERR_HIP = -6,       /* the HIP runtime reported a launch error */
+  ROPE_ATTN_ERR_ARG = -7        /* base not finite and > 0, or causal not 0/1 */
+} rope_attn_status;
+
+/* Workspace (device memory, 256-byte aligned recommended) needed by
+ * rope_attn_fwd for these arguments; 0 on invalid arguments. */
+size_t rope_attn_fwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal);
+
+/* Forward.  q, k, v: [B,H,N,D] inputs of `dtype`; o: [B,H,N,D] float32
+ * output; lse: [B,H,N] float32 output (natural log, scale included).
+ * alpha: [D/2] float32 device pointer, or NULL for alpha = 0 (standard
+ * RoPE).  base: RoPE base b > 0.  causal: 1 = keys j <= i, 0 = all keys. */
+int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+                  int N, int D, int dtype, double base, const float* alpha, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by rope_attn_bwd; 0 on invalid arguments. */
+size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal);
+
+/* Backward.  q, k, v, dO: [B,H,N,D] of `dtype`; o, lse: the forward's float32
+ * outputs for the same q, k, v, base, alpha, causal.  dq, dk, dv: [B,H,N,D]
+ * float32 outputs (un-rotated frame).  dalpha: [D/2] float32 output, or
+ * NULL to skip it. */
+int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, const void* dO,
+                  const float* lse, float* dq, float* dk, float* dv, float* dalpha, int B, int H,
+                  int N, int D, int dtype, double base, const float* alpha, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rope_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_ATTN_H */

@@ -1,0 +1,56 @@
+"""Shared helpers of the GPU tests: move seeded inputs to the device, run the
+HIP path through the C ABI binding, compare with the float64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+from bwd_rope_apply_amd import workloads as W
+
+
+def to_device(x: np.ndarray, device="cuda"):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def run_gpu(inp: W.Inputs, causal=None, alpha=True, want_dalpha=True):
+    """Forward and backward on the GPU; returns float64 numpy arrays."""
+    import torch
+    from bwd_rope_apply_amd import fwd, bwd
+    wl = inp.wl
+    causal = wl.causal if causal is None else causal
+    q, k, v, do = (to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    a = to_device(inp.alpha) if alpha else None
+    o, lse = fwd(q, k, v, wl.base, a, causal)
+    dq, dk, dv, da = bwd(q, k, v, o, do, lse, wl.base, a, causal, want_dalpha=want_dalpha)
+    torch.cuda.synchronize()
+    out = dict(O=o, LSE=lse, dQ=dq, dK=dk, dV=dv, dalpha=da)
+    return {n: (None if t is None else t.double().cpu().numpy()) for n, t in out.items()}
+
+
+def run_oracle(inp: W.Inputs, causal=None, alpha=True):
+    from oracle import ref
+    wl = inp.wl
+    causal = wl.causal if causal is None else causal
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    a = inp.alpha if alpha else None
+    o, lse = ref.ref_fwd(q, k, v, wl.base, a, causal)
+    dq, dk, dv, da = ref.ref_bwd(q, k, v, o, do, lse, wl.base, a, causal)
+    return dict(O=o, LSE=lse, dQ=dq, dK=dk, dV=dv, dalpha=da)
+
+
+def err_rms(got, ref) -> float:
+    """max |got - ref| / rms(ref)  (bf16 inputs: the bar is 2e-2)."""
+    rms = float(np.sqrt(np.mean(np.square(ref))))
+    return float(np.max(np.abs(got - ref))) / max(rms, 1e-30)
+
+
+def err_rel(got, ref) -> float:
+    """max |got - ref| / max |ref|  (fp32 inputs: the bar is 1e-4)."""
+    return float(np.max(np.abs(got - ref))) / max(float(np.max(np.abs(ref))), 1e-30)
+
+
+def report(got, ref, names=("O", "dQ", "dK", "dV", "dalpha")):
+    return {n: (err_rms(got[n], ref[n]), err_rel(got[n], ref[n])) for n in names
+            if got.get(n) is not None}

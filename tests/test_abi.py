@@ -1,0 +1,81 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/rope_attn.h declares, and rejects invalid arguments before any HIP
+call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rope_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rope_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bwd_rope_apply_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("librope_attn.so is not built: run `python -m bwd_rope_apply_amd.build`")
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == ["rope_attn_bwd", "rope_attn_bwd_workspace_bytes", "rope_attn_fwd",
+                           "rope_attn_fwd_workspace_bytes", "rope_attn_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_queries(lib):
+    assert lib.rope_attn_fwd_workspace_bytes(1, 32, 8192, 128, 1, 1) > 0
+    assert lib.rope_attn_bwd_workspace_bytes(1, 32, 8192, 128, 1, 1) > 0
+    assert lib.rope_attn_fwd_workspace_bytes(1, 1, 16, 96, 1, 1) == 0   # bad D
+    assert lib.rope_attn_bwd_workspace_bytes(0, 1, 16, 64, 1, 1) == 0   # bad B
+    assert lib.rope_attn_bwd_workspace_bytes(1, 1, 16, 64, 7, 1) == 0   # bad dtype
+
+
+A = 4096  # any 16-byte aligned non-null value; validation fails before use
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, A, 1 << 30, None), -1),
+    ((A, A, A, A, A, 1, 1, 16, 96, 1, 1e4, None, 1, A, 1 << 30, None), -2),
+    ((A, A, A, A, A, 1, 0, 16, 64, 1, 1e4, None, 1, A, 1 << 30, None), -2),
+    ((A, A, A, A, A, 1, 1, 16, 64, 5, 1e4, None, 1, A, 1 << 30, None), -3),
+    ((A + 2, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, A, 1 << 30, None), -4),
+    ((A, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, A, 16, None), -5),
+    ((A, A, A, A, A, 1, 1, 16, 64, 1, 0.0, None, 1, A, 1 << 30, None), -7),
+    ((A, A, A, A, A, 1, 1, 16, 64, 1, float("nan"), None, 1, A, 1 << 30, None), -7),
+    ((A, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 2, A, 1 << 30, None), -7),
+    ((A, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, None, 1 << 30, None), -1),
+])
+def test_fwd_validation(lib, args, status):
+    assert lib.rope_attn_fwd(*args) == status
+
+
+def test_bwd_validation(lib):
+    ok = [A] * 10 + [1, 1, 16, 64, 1, 1e4, None, 1, A, 1 << 30, None]
+    bad = list(ok)
+    bad[6] = None  # dq
+    assert lib.rope_attn_bwd(*bad) == -1
+    bad = list(ok)
+    bad[9] = A + 4  # dalpha misaligned
+    assert lib.rope_attn_bwd(*bad) == -4
+    bad = list(ok)
+    bad[19] = 8  # workspace too small
+    assert lib.rope_attn_bwd(*bad) == -5
+
+
+def test_status_strings(lib):
+    for s in range(-7, 1):
+        assert lib.rope_attn_status_string(s)
+    assert lib.rope_attn_status_string(-99) == b"unknown status"

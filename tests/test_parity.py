@@ -1,0 +1,130 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle,
+element by element on the same seeded inputs.
+
+Bars: fp32 inputs, max |err| / max |ref| <= 1e-4 per tensor; bf16 inputs,
+max |err| / rms(ref) <= 2e-2 per tensor (O, dQ, dK, dV, dalpha) and LSE
+within 2e-2 absolute.  Sizes span several 128-row tiles, a ragged tail,
+the exact corner and the degenerate N = 1.
+"""
+import numpy as np
+import pytest
+
+from bwd_rope_apply_amd import workloads as W
+import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+NAMES = ("O", "dQ", "dK", "dV", "dalpha")
+
+
+def _check(inp, causal=None, alpha=True):
+    got = Hn.run_gpu(inp, causal, alpha)
+    ref = Hn.run_oracle(inp, causal, alpha)
+    for n in NAMES + ("LSE",):
+        assert np.isfinite(got[n]).all(), n
+    if inp.wl.dtype == "fp32":
+        errs = {n: Hn.err_rel(got[n], ref[n]) for n in NAMES}
+        errs["LSE"] = float(np.max(np.abs(got["LSE"] - ref["LSE"])))
+        print(inp.wl.name, errs)
+        for n, e in errs.items():
+            assert e <= FP32_TOL, (n, e)
+    else:
+        errs = {}
+        for n in NAMES:
+            if np.sqrt(np.mean(np.square(ref[n]))) < 1e-12:
+                # identically zero by the mathematics (N = 1: dQ = dK = 0,
+                # dalpha = 0): compare absolutely against fp32 rounding of
+                # equal dot products
+                errs[n + "_abs"] = float(np.max(np.abs(got[n])))
+            else:
+                errs[n] = Hn.err_rms(got[n], ref[n])
+        errs["LSE"] = float(np.max(np.abs(got["LSE"] - ref["LSE"])))
+        print(inp.wl.name, errs)
+        for n, e in errs.items():
+            assert e <= (1e-5 if n.endswith("_abs") else BF16_TOL), (n, e)
+    return got, ref
+
+
+def test_tiny_fp32_workload():
+    """B1 H1 N128 D64 fp32, causal, b = 1e4, alpha = 0, U[-1, 1]."""
+    _check(W.make_inputs(W.get("tiny_fp32")))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_ragged(causal, D):
+    wl = W.Workload("fp32_ragged", 2, 3, 200, D, "fp32", 500.0, causal, ("normal", 1.0, 1.0),
+                    ("normal", 1.0, 1.0), ("normal", 1.0, 1.0), ("normal", 0.3, 1.0), seed=77)
+    _check(W.make_inputs(wl))
+
+
+@pytest.mark.parametrize("name", ["layer_2k", "train_4k", "long_8k", "vlong_32k"])
+def test_bf16_workloads_reduced_length(name):
+    """Each bf16 workload's distributions at N = 700 (corner + several
+    128-row tiles + ragged tail), 3 heads."""
+    _check(W.make_inputs(W.get(name, B=1, H=3, N=700)))
+
+
+@pytest.mark.parametrize("N", [1, 5, 77, 128, 129, 255, 256, 383])
+def test_bf16_lengths(N):
+    _check(W.make_inputs(W.get("layer_2k", B=2, H=2, N=N, seed=500 + N)))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_noncausal(D):
+    wl = W.Workload("bf16_full", 1, 2, 333, D, "bf16", 1e4, False, ("normal", 1.0, 1.0),
+                    ("normal", 1.0, 1.0), ("normal", 1.0, 1.0), ("normal", 0.2, 1.0), seed=91)
+    _check(W.make_inputs(wl), causal=False)
+
+
+def test_bf16_standard_rope_alpha_null():
+    """alpha = NULL means alpha = 0 (standard RoPE)."""
+    _check(W.make_inputs(W.get("long_8k", B=1, H=2, N=400)), alpha=False)
+
+
+def test_deterministic_and_overwrites_nan():
+    """Two runs are bit-identical (no float atomics) and NaN-filled output
+    buffers are fully overwritten."""
+    import torch
+    from bwd_rope_apply_amd import fwd, bwd
+    inp = W.make_inputs(W.get("layer_2k", B=1, H=2, N=450))
+    q, k, v, do = (Hn.to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    a = Hn.to_device(inp.alpha)
+    outs = []
+    for _ in range(2):
+        o = torch.full((1, 2, 450, 128), float("nan"), device="cuda")
+        lse = torch.full((1, 2, 450), float("nan"), device="cuda")
+        fwd(q, k, v, 1e4, a, True, out=(o, lse))
+        g = [torch.full_like(o, float("nan")) for _ in range(3)] + [
+            torch.full((64,), float("nan"), device="cuda")]
+        bwd(q, k, v, o, do, lse, 1e4, a, True, out=tuple(g))
+        torch.cuda.synchronize()
+        outs.append([o, lse] + g)
+    for x, y in zip(*outs):
+        assert torch.isfinite(x).all()
+        assert torch.equal(x, y)
+
+
+def test_rotational_balance_on_gpu_gradients():
+    """Per (b, h, m): sum_i wedge(q_i, dQ_i) + sum_j wedge(k_j, dK_j) = 0 holds
+    for the GPU's own dQ, dK (a property, no oracle)."""
+    inp = W.make_inputs(W.get("long_8k", B=1, H=2, N=600))
+    got = Hn.run_gpu(inp)
+    q, k = inp.f64("q"), inp.f64("k")
+    wq = (q[..., 0::2] * got["dQ"][..., 1::2] - q[..., 1::2] * got["dQ"][..., 0::2]).sum(2)
+    wk = (k[..., 0::2] * got["dK"][..., 1::2] - k[..., 1::2] * got["dK"][..., 0::2]).sum(2)
+    scale = np.abs(q[..., 0::2] * got["dQ"][..., 1::2]).sum(2).max()
+    assert np.abs(wq + wk).max() <= 1e-3 * scale
+
+
+def test_invalid_arguments_raise():
+    import torch
+    from bwd_rope_apply_amd import fwd, RopeAttnError
+    q = torch.zeros((1, 1, 16, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RopeAttnError):
+        fwd(q, q, q, 1e4, None, True)
+    q = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RopeAttnError):
+        fwd(q, q, q, -1.0, None, True)
