@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Throughput of exact causal RoPE attention, forward + backward (dQ, dK, dV
+and d alpha), on one MI355X, through the library's C ABI.
+
+One step = the forward pass and the backward pass of the whole workload
+(default: B=1, H=32, N=8192, D=128, bf16 inputs, causal, base 1e4, alpha ~
+U[-1, 0.5]) with inputs resident in device memory.  Prints one JSON line.
+
+Throughput is algorithmic: 6 B H N^2 D flops per step (the two forward
+products and the four backward products over the causal half), the standard
+count for causal attention training; recomputation of scores in the backward
+is not counted.  Per-stage durations come from HIP events recorded on the
+stream the library launches on (torch's current stream), between the staged
+entry points, so the timed work is exactly the full forward + backward.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_TFLOPS = 2516.6   # fp16 / bf16 dense matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
+HBM_GBS = 8000.0
+METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
+
+FWD_STAGES = [("fwd_prep", 1), ("fwd_exact", 2), ("fwd_main", 4)]
+BWD_STAGES = [("bwd_prep", 1), ("bwd_exact", 2), ("bwd_dq", 8), ("bwd_dkdv", 16),
+              ("bwd_dalpha", 32)]
+# algorithmic products carried by each matrix-core stage (units of B H N^2 D
+# flops, causal): fwd QK^T and PV; dQ; dV, dP and dK
+STAGE_FLOP_UNITS = {"fwd_main": 2.0, "bwd_dq": 1.0, "bwd_dkdv": 3.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, wl):
+    """The float64 oracle on one head of the same inputs (a bounded sample),
+    timed on the host cores, scaled to TFLOP/s with the same flop count."""
+    import numpy as np
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    full = {n: inp.f64(n).reshape(-1, 1, wl.N, wl.D) for n in ("q", "k", "v", "do")}
+
+    def run(heads):
+        q, k, v, do = (full[n][:heads].reshape(1, heads, wl.N, wl.D) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        o, lse = ref.ref_fwd(q, k, v, wl.base, inp.alpha, wl.causal)
+        ref.ref_bwd(q, k, v, o, do, lse, wl.base, inp.alpha, wl.causal)
+        return time.perf_counter() - t0
+
+    # size the sample to about 10 s of oracle work (at least one head)
+    t1 = run(1)
+    heads = int(min(wl.B * wl.H, max(1, round(10.0 / max(t1, 1e-3)))))
+    dt = run(heads) if heads > 1 else t1
+    flops = 6.0 * heads * wl.N * wl.N * wl.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {wl.B * wl.H} heads (N={wl.N}, D={wl.D}), float64 fwd+bwd incl. "
+                      f"dalpha, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads are independent, a multi-GPU run would shard them and all-reduce dalpha)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bwd_rope_apply_amd import workloads as W
+    from bwd_rope_apply_amd import _lib
+
+    wl = W.get(args.workload)
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+
+    def dev_t(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v, do = (dev_t(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    alpha = dev_t(inp.alpha)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    f32 = dict(dtype=torch.float32, device=dev)
+    o, lse = torch.empty((B, H, N, D), **f32), torch.empty((B, H, N), **f32)
+    dq, dk, dv = (torch.empty((B, H, N, D), **f32) for _ in range(3))
+    da = torch.empty((D // 2,), **f32)
+    dt_code = _lib.BF16 if wl.dtype == "bf16" else _lib.FP32
+    ws_f = torch.empty(_lib.workspace_bytes("fwd", B, H, N, D, dt_code, wl.causal), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(_lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal), dtype=torch.uint8, device=dev)
+
+    names = [n for n, _ in FWD_STAGES] + [n for n, _ in BWD_STAGES]
+
+    def step(events=None):
+        i = 0
+        for name, bit in FWD_STAGES:
+            if events is not None:
+                events[i].record()
+            _lib.fwd(q, k, v, wl.base, alpha, wl.causal, workspace=ws_f, out=(o, lse), stages=bit)
+            i += 1
+        for name, bit in BWD_STAGES:
+            if events is not None:
+                events[i].record()
+            _lib.bwd(q, k, v, o, do, lse, wl.base, alpha, wl.causal, workspace=ws_b,
+                     out=(dq, dk, dv, da), stages=bit)
+            i += 1
+        if events is not None:
+            events[i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not (torch.isfinite(o).all() and torch.isfinite(dq).all() and torch.isfinite(dk).all()
+            and torch.isfinite(dv).all() and torch.isfinite(da).all()):
+        print("bench.py: non-finite outputs", file=sys.stderr)
+        sys.exit(1)
+
+    stage_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+    unit = float(B) * H * N * N * D
+    flops = 6.0 * unit
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    dom = max(STAGE_FLOP_UNITS, key=lambda n: stage_ms[n])
+    dom_flops = STAGE_FLOP_UNITS[dom] * unit
+    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get(dom)
+    kernel = {"fwd_main": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}[dom]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16" if wl.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
+                   "base": wl.base, "storage": wl.dtype, "outputs": "fp32",
+                   "flops_per_step": flops, "pct_bf16_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic, "avg_ms": round(stage_ms[dom], 4)},
+        "stages_ms": {n: round(t, 4) for n, t in stage_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

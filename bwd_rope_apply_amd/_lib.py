@@ -16,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librope_attn.so")
 
 FP32, BF16 = 0, 1
+# rope_attn_stage bits
+STAGE_PREP, STAGE_EXACT, STAGE_MAIN, STAGE_DQ, STAGE_DKDV, STAGE_DALPHA = 1, 2, 4, 8, 16, 32
+STAGE_ALL = 63
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_HIP", -7: "ERR_ARG"}
 
@@ -46,6 +49,10 @@ def load() -> ctypes.CDLL:
     lib.rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, vp, i,
                                   vp, sz, vp]
     lib.rope_attn_bwd.restype = i
+    lib.rope_attn_fwd_stages.argtypes = [ctypes.c_uint] + lib.rope_attn_fwd.argtypes
+    lib.rope_attn_fwd_stages.restype = i
+    lib.rope_attn_bwd_stages.argtypes = [ctypes.c_uint] + lib.rope_attn_bwd.argtypes
+    lib.rope_attn_bwd_stages.restype = i
     lib.rope_attn_status_string.argtypes = [i]
     lib.rope_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -105,8 +112,9 @@ def workspace_bytes(kind: str, B: int, H: int, N: int, D: int, dtype: int, causa
 
 
 def fwd(q, k, v, base: float, alpha=None, causal: bool = True, workspace=None,
-        out: Optional[Tuple] = None):
-    """O [B,H,N,D] float32 and LSE [B,H,N] float32 for rotated attention."""
+        out: Optional[Tuple] = None, stages: int = STAGE_ALL):
+    """O [B,H,N,D] float32 and LSE [B,H,N] float32 for rotated attention.
+    ``stages`` selects rope_attn_fwd_stages bits (default: the whole pass)."""
     import torch
     lib = load()
     B, H, N, D = _shape(q, k, v)
@@ -120,16 +128,17 @@ def fwd(q, k, v, base: float, alpha=None, causal: bool = True, workspace=None,
     nbytes = workspace_bytes("fwd", B, H, N, D, dt, causal)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.rope_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D, dt,
-                           float(base), _ptr(alpha), int(causal), _ptr(workspace),
-                           workspace.numel(), _stream(q.device))
+    st = lib.rope_attn_fwd_stages(stages, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                                  D, dt, float(base), _ptr(alpha), int(causal), _ptr(workspace),
+                                  workspace.numel(), _stream(q.device))
     _check("rope_attn_fwd", st)
     return o, lse
 
 
 def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, workspace=None,
-        want_dalpha: bool = True, out: Optional[Tuple] = None):
-    """(dQ, dK, dV [B,H,N,D] float32, dalpha [D/2] float32 or None)."""
+        want_dalpha: bool = True, out: Optional[Tuple] = None, stages: int = STAGE_ALL):
+    """(dQ, dK, dV [B,H,N,D] float32, dalpha [D/2] float32 or None).
+    ``stages`` selects rope_attn_bwd_stages bits (default: the whole pass)."""
     import torch
     lib = load()
     B, H, N, D = _shape(q, k, v)
@@ -151,9 +160,9 @@ def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, works
     nbytes = workspace_bytes("bwd", B, H, N, D, dt, causal)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.rope_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                           _ptr(dk), _ptr(dv), _ptr(da), B, H, N, D, dt, float(base),
-                           _ptr(alpha), int(causal), _ptr(workspace), workspace.numel(),
-                           _stream(q.device))
+    st = lib.rope_attn_bwd_stages(stages, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), B, H, N, D, dt,
+                                  float(base), _ptr(alpha), int(causal), _ptr(workspace),
+                                  workspace.numel(), _stream(q.device))
     _check("rope_attn_bwd", st)
     return dq, dk, dv, da

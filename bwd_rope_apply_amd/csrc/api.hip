@@ -67,7 +67,8 @@ Layout layout(const Shape& s, bool bwd) {
     if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * CORNER * s.D);
     if (s.bf16()) {
       const MfmaParams m = mfma_base(s);
-      L.slots = (s.corner() ? simt_slots((int)s.bh(), CORNER) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
+      L.slots = (s.corner() ? simt_slots((int)s.bh(), s.corner()) : 0) + dq_mfma_slots(m) +
+                dkdv_mfma_slots(m);
     } else {
       L.slots = 2 * simt_slots((int)s.bh(), s.N);
     }
@@ -125,9 +126,10 @@ size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int 
   return layout(s, true).total();
 }
 
-int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
-                  int N, int D, int dtype, double base, const float* alpha, int causal,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const void* v, float* o,
+                         float* lse, int B, int H, int N, int D, int dtype, double base,
+                         const float* alpha, int causal, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   const Shape s{B, H, N, D, dtype, causal};
   if (!q || !k || !v || !o || !lse) return ROPE_ATTN_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
@@ -144,35 +146,44 @@ int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* 
   half_t* qh = c.take<half_t>(L.qh);
   half_t* kh = c.take<half_t>(L.kh);
   half_t* vh = c.take<half_t>(L.vh);
-  tables(s, base, alpha, theta, cs, hs);
 
-  SimtParams sp = {};
-  sp.q = q; sp.k = k; sp.v = v; sp.cs = cs; sp.out_o = o; sp.out_lse = lse;
-  sp.bf16 = s.bf16(); sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
-  sp.scale = 1.0f / sqrtf((float)D);
-  if (!s.bf16()) {
-    sp.rows = N;
-    launch_simt_fwd(sp, hs);
-    return finish();
+  if (stages & ROPE_ATTN_STAGE_PREP) {
+    tables(s, base, alpha, theta, cs, hs);
+    if (s.bf16()) {
+      PrepParams pp = {};
+      pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
+      pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
+      launch_prep(pp, hs);
+    }
   }
-  PrepParams pp = {};
-  pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
-  pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
-  launch_prep(pp, hs);
-  if (s.corner()) {
-    sp.rows = CORNER;
-    launch_simt_fwd(sp, hs);
+  if (stages & ROPE_ATTN_STAGE_EXACT) {
+    SimtParams sp = {};
+    sp.q = q; sp.k = k; sp.v = v; sp.cs = cs; sp.out_o = o; sp.out_lse = lse;
+    sp.bf16 = s.bf16(); sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
+    sp.scale = 1.0f / sqrtf((float)D);
+    sp.rows = s.bf16() ? s.corner() : N;
+    if (sp.rows) launch_simt_fwd(sp, hs);
   }
-  MfmaParams mp = mfma_base(s);
-  mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.o = o; mp.out_lse = lse;
-  launch_fwd_mfma(mp, hs);
+  if ((stages & ROPE_ATTN_STAGE_MAIN) && s.bf16()) {
+    MfmaParams mp = mfma_base(s);
+    mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.o = o; mp.out_lse = lse;
+    launch_fwd_mfma(mp, hs);
+  }
   return finish();
 }
 
-int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, const void* dO,
-                  const float* lse, float* dq, float* dk, float* dv, float* dalpha, int B, int H,
+int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
                   int N, int D, int dtype, double base, const float* alpha, int causal,
                   void* workspace, size_t workspace_bytes, void* stream) {
+  return rope_attn_fwd_stages(ROPE_ATTN_STAGE_ALL, q, k, v, o, lse, B, H, N, D, dtype, base, alpha,
+                              causal, workspace, workspace_bytes, stream);
+}
+
+int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const void* v,
+                         const float* o, const void* dO, const float* lse, float* dq, float* dk,
+                         float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
+                         double base, const float* alpha, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   const Shape s{B, H, N, D, dtype, causal};
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ROPE_ATTN_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dO) ||
@@ -195,54 +206,65 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
   float* dkp = c.take<float>(L.dkp);
   float* dvp = c.take<float>(L.dvp);
   float* part = c.take<float>(L.part);
-  tables(s, base, alpha, theta, cs, hs);
 
-  PrepParams pp = {};
-  pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
-  pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
-  pp.bf16 = s.bf16(); pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
-  launch_prep(pp, hs);
+  // d alpha partial slots: [exact dQ rows | exact dK rows | MFMA dQ | MFMA dK]
+  const int BHi = (int)s.bh();
+  const int exact_rows = s.bf16() ? s.corner() : N;
+  const int n_exact_dq = exact_rows ? simt_slots(BHi, exact_rows) : 0;
+  const int n_exact_dk = s.bf16() ? 0 : simt_slots(BHi, N);
+  MfmaParams mp = mfma_base(s);
+  const int n_dq = s.bf16() ? dq_mfma_slots(mp) : 0;
+  const int n_dk = s.bf16() ? dkdv_mfma_slots(mp) : 0;
 
-  SimtParams sp = {};
-  sp.q = q; sp.k = k; sp.v = v; sp.dO = dO; sp.o = o; sp.lse = lse; sp.drow = drow; sp.cs = cs;
-  sp.dq = dq; sp.dk = dk; sp.dv = dv; sp.dk_part = dkp; sp.dv_part = dvp;
-  sp.dalpha_part = part;
-  sp.bf16 = s.bf16(); sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
-  sp.scale = 1.0f / sqrtf((float)D);
-  int slot = 0;
-  if (!s.bf16()) {
-    sp.rows = N; sp.qend = N; sp.final_ = 1;
-    sp.slot0 = slot;
-    launch_simt_dq(sp, hs);
-    slot += simt_slots((int)s.bh(), N);
-    sp.slot0 = slot;
-    launch_simt_dkdv(sp, hs);
-    slot += simt_slots((int)s.bh(), N);
-  } else {
-    if (s.corner()) {
-      sp.rows = CORNER; sp.qend = N < CORNER ? N : CORNER; sp.final_ = 0;
-      sp.slot0 = slot;
-      launch_simt_dq(sp, hs);
-      slot += simt_slots((int)s.bh(), CORNER);
-      launch_simt_dkdv(sp, hs);  // rotated-frame partials, no d alpha slots
-    }
-    MfmaParams mp = mfma_base(s);
-    mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.q = q; mp.k = k; mp.cs = cs;
-    mp.lse = lse; mp.drow = drow; mp.dq = dq; mp.dk = dk; mp.dv = dv;
-    mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
-    mp.slot0 = slot;
-    launch_dq_mfma(mp, hs);
-    slot += dq_mfma_slots(mp);
-    mp.slot0 = slot;
-    launch_dkdv_mfma(mp, hs);
-    slot += dkdv_mfma_slots(mp);
+  if (stages & ROPE_ATTN_STAGE_PREP) {
+    tables(s, base, alpha, theta, cs, hs);
+    PrepParams pp = {};
+    pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
+    pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
+    pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
+    launch_prep(pp, hs);
   }
-  if (dalpha) {
+  if ((stages & ROPE_ATTN_STAGE_EXACT) && exact_rows) {
+    SimtParams sp = {};
+    sp.q = q; sp.k = k; sp.v = v; sp.dO = dO; sp.o = o; sp.lse = lse; sp.drow = drow; sp.cs = cs;
+    sp.dq = dq; sp.dk = dk; sp.dv = dv; sp.dk_part = dkp; sp.dv_part = dvp;
+    sp.dalpha_part = part;
+    sp.bf16 = s.bf16(); sp.BH = BHi; sp.N = N; sp.D = D; sp.causal = causal;
+    sp.scale = 1.0f / sqrtf((float)D);
+    sp.rows = exact_rows;
+    sp.qend = exact_rows < N ? exact_rows : N;
+    sp.final_ = s.bf16() ? 0 : 1;  // bf16: rotated-frame corner partials for the MFMA pass
+    sp.slot0 = 0;
+    launch_simt_dq(sp, hs);
+    sp.slot0 = n_exact_dq;
+    launch_simt_dkdv(sp, hs);
+  }
+  mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.q = q; mp.k = k; mp.cs = cs;
+  mp.lse = lse; mp.drow = drow; mp.dq = dq; mp.dk = dk; mp.dv = dv;
+  mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
+  if ((stages & ROPE_ATTN_STAGE_DQ) && s.bf16()) {
+    mp.slot0 = n_exact_dq + n_exact_dk;
+    launch_dq_mfma(mp, hs);
+  }
+  if ((stages & ROPE_ATTN_STAGE_DKDV) && s.bf16()) {
+    mp.slot0 = n_exact_dq + n_exact_dk + n_dq;
+    launch_dkdv_mfma(mp, hs);
+  }
+  if ((stages & ROPE_ATTN_STAGE_DALPHA) && dalpha) {
     DalphaParams dp = {};
-    dp.part = part; dp.theta_hat = theta; dp.dalpha = dalpha; dp.slots = slot; dp.D = D;
+    dp.part = part; dp.theta_hat = theta; dp.dalpha = dalpha;
+    dp.slots = n_exact_dq + n_exact_dk + n_dq + n_dk; dp.D = D;
     launch_dalpha_reduce(dp, hs);
   }
   return finish();
+}
+
+int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, const void* dO,
+                  const float* lse, float* dq, float* dk, float* dv, float* dalpha, int B, int H,
+                  int N, int D, int dtype, double base, const float* alpha, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return rope_attn_bwd_stages(ROPE_ATTN_STAGE_ALL, q, k, v, o, dO, lse, dq, dk, dv, dalpha, B, H,
+                              N, D, dtype, base, alpha, causal, workspace, workspace_bytes, stream);
 }
 
 const char* rope_attn_status_string(int status) {

@@ -58,36 +58,30 @@ __device__ __forceinline__ void map_block(int idx, int BH, int ntiles, bool heav
   t = heavy_high ? ntiles - 1 - k : k;
 }
 
+// Register copy of one streamed [BN][D] fp16 tile: every thread holds NCH
+// 16-byte chunks (row = chunk / (D/8)).  Rows at or past N are clamped to
+// N - 1: they are masked downstream, so they only need to be finite.
 template <int D>
-__device__ __forceinline__ void stage_rows(half_t* dst, const half_t* src, int r0, int N) {
-  // dst: [BN][D + 8] natural copy of rows r0..r0+BN (zero past N)
-  constexpr int CPR = D / 8, LD = D + 8;
-  for (int ch = threadIdx.x; ch < BN * CPR; ch += 256) {
-    const int r = ch / CPR, c8 = ch % CPR;
-    half8 x = {};
-    if (r0 + r < N) x = *reinterpret_cast<const half8*>(src + (size_t)(r0 + r) * D + c8 * 8);
-    *reinterpret_cast<half8*>(dst + r * LD + c8 * 8) = x;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void stage_rows_t(half_t* dst, const half_t* src, int r0, int N) {
-  // dst: [D][BN + 8] transposed copy of rows r0..r0+BN; each lane moves two
-  // consecutive rows so the LDS writes are whole dwords.
-  constexpr int LDT = BN + 8;
-  for (int ch = threadIdx.x; ch < (BN / 2) * (D / 8); ch += 256) {
-    const int kp = ch % (BN / 2), c8 = ch / (BN / 2);
-    const int r = 2 * kp;
-    half8 a = {}, b = {};
-    if (r0 + r < N) a = *reinterpret_cast<const half8*>(src + (size_t)(r0 + r) * D + c8 * 8);
-    if (r0 + r + 1 < N) b = *reinterpret_cast<const half8*>(src + (size_t)(r0 + r + 1) * D + c8 * 8);
+struct TileRegs {
+  static constexpr int CPR = D / 8;
+  static constexpr int NCH = BN * CPR / 256;
+  half8 x[NCH];
+  __device__ __forceinline__ void load(const half_t* src, int r0, int N) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      half2v v2 = {a[e], b[e]};
-      *reinterpret_cast<half2v*>(dst + (c8 * 8 + e) * LDT + r) = v2;
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + 256 * i;
+      const int row = min(r0 + ch / CPR, N - 1);
+      x[i] = *reinterpret_cast<const half8*>(src + (size_t)row * D + (ch % CPR) * 8);
     }
   }
-}
+  __device__ __forceinline__ void store(half_t* dst) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + 256 * i;
+      *reinterpret_cast<half8*>(dst + (ch / CPR) * (D + 8) + (ch % CPR) * 8) = x[i];
+    }
+  }
+};
 
 template <int D>
 __device__ __forceinline__ void load_frag_rows(half8* f, const half_t* src, int row, int N, int g) {
@@ -125,17 +119,35 @@ __device__ __forceinline__ void to_frags(const f32x16* s, half8* f) {
   }
 }
 
-// acc[cb] += A(lds rows 32cb + l32, 16-key steps) * frag  (A read from a
-// transposed [D][BN + 8] tile).
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+
+__device__ __forceinline__ s16x4 ds_read_tr(const half_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// acc[cb] += X^T(columns 32cb.., rows = 16-wide k steps) * frag, with X the
+// natural [BN][D + 8] tile in LDS.  ds_read_b64_tr_b16 transposes a 4 x 16
+// block per 16-lane group (lane j receives element j of the 4 rows that
+// lanes 4e + j/4 point at), so lane s of a group points at row s/4, columns
+// 4 (s % 4) .. +3 of its block, and two reads give the 8 k-values (rows
+// 16t + 8g + 0..7) of column 32cb + l32.
 template <int D>
-__device__ __forceinline__ void accumulate_t(f32x16* acc, const half_t* ldt, const half8* f, int l32,
-                                             int g) {
-  constexpr int LDT = BN + 8;
+__device__ __forceinline__ void accumulate_tr(f32x16* acc, const half_t* lds, const half8* f, int lane) {
+  constexpr int LD = D + 8;
+  const int s16 = lane & 15, g = lane >> 5;
+  const half_t* base = lds + (8 * g + (s16 >> 2)) * LD + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) {
-    const half_t* row = ldt + (32 * cb + l32) * LDT + 8 * g;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[cb] = mfma(*reinterpret_cast<const half8*>(row + 16 * t), f[t], acc[cb]);
+    for (int t = 0; t < 4; ++t) {
+      const half_t* p = base + 16 * t * LD + 32 * cb;
+      const s16x4 lo = ds_read_tr(p), hi = ds_read_tr(p + 4 * LD);
+      typedef __attribute__((ext_vector_type(8))) short s16x8;
+      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const half8 a = __builtin_bit_cast(half8, both);
+      acc[cb] = mfma(a, f[t], acc[cb]);
+    }
   }
 }
 
@@ -194,12 +206,129 @@ __device__ __forceinline__ void finish_rows(f32x16* acc, float scale, const floa
   }
 }
 
+// One 64-key step of the forward for one wave: scores, online softmax
+// (running max m and sum l per query, in log2 units), O += P V.  MASK hides
+// keys after klim (causal diagonal, ragged tail).
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_tile(f32x16* o, float& m, float& l, const half_t* Ks,
+                                         const half_t* Vs, const half8* qf, int k0, int klim,
+                                         float c2, int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  f32x16 s[2];
+  scores<D>(s, Ks, qf, l32, g);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[mb][r] * c2;
+      if (MASK) {
+        const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7);
+        x = key > klim ? -INFINITY : x;
+      }
+      s[mb][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float mn = fmaxf(m, mx);
+  const float ms = (mn == -INFINITY) ? 0.f : mn;
+  const float alpha = exp2_fast(m - ms);
+  float ls = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = exp2_fast(s[mb][r] - ms);
+      s[mb][r] = pr;
+      ls += pr;
+    }
+  }
+  l = l * alpha + ls;
+  m = mn;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
+  half8 pf[4];
+  to_frags(s, pf);
+  accumulate_tr<D>(o, Vs, pf, lane);
+}
+
+// One 64-key step of dQ for one wave: recompute P from the LSE,
+// dP = dO V^T, dS = P o (dP - D), dQ~ += dS K~.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const half_t* Vs,
+                                        const half8* qf, const half8* df, int k0, int klim,
+                                        float c2, float lse2, float dr, int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  f32x16 s[2], dp[2];
+  scores<D>(s, Ks, qf, l32, g);
+  scores<D>(dp, Vs, df, l32, g);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = exp2_fast(s[mb][r] * c2 - lse2);
+      if (MASK) {
+        const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7);
+        pr = key > klim ? 0.f : pr;
+      }
+      s[mb][r] = pr * (dp[mb][r] - dr);
+    }
+  }
+  half8 sf[4];
+  to_frags(s, sf);
+  accumulate_tr<D>(acc, Ks, sf, lane);
+}
+
+// One 64-query step of dK, dV for one wave (this lane's key along n):
+// P = exp(S - LSE), dV += P^T dO, dP = dO V^T, dS = P o (dP - D),
+// dK~ += dS^T Q~.  MASK hides queries before this lane's key.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* Qs,
+                                          const half_t* Ds, const float* lses, const float* drs,
+                                          const half8* kf, const half8* vf, int r0, int key,
+                                          float c2, int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  f32x16 s[2], dp[2];
+  scores<D>(s, Qs, kf, l32, g);
+  scores<D>(dp, Ds, vf, l32, g);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ql = 32 * mb + 16 * h + 8 * g;
+      const float4 la = *reinterpret_cast<const float4*>(lses + ql);
+      const float4 lb = *reinterpret_cast<const float4*>(lses + ql + 4);
+      const float4 da = *reinterpret_cast<const float4*>(drs + ql);
+      const float4 db = *reinterpret_cast<const float4*>(drs + ql + 4);
+      const float lv8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * h + e;
+        float pr = exp2_fast(s[mb][r] * c2 - lv8[e]);
+        if (MASK) pr = key > r0 + ql + e ? 0.f : pr;
+        s[mb][r] = pr;
+        dp[mb][r] = pr * (dp[mb][r] - dv8[e]);
+      }
+    }
+  }
+  half8 pf[4], sf[4];
+  to_frags(s, pf);
+  to_frags(dp, sf);
+  accumulate_tr<D>(dv, Ds, pf, lane);
+  accumulate_tr<D>(dk, Qs, sf, lane);
+}
+
 // ------------------------------------------------------------------ forward
+// Workgroup = 128 query rows of one head (4 waves x 32 rows); the loop
+// streams 64-key tiles of K~ and V through double-buffered LDS, the next
+// tile's global loads in flight while the current tile is computed.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_kernel(MfmaParams p) {
-  constexpr int DT = D / 16, CB = D / 32, KLD = D + 8, VLD = BN + 8;
-  __shared__ __attribute__((aligned(16))) half_t Ks[BN * KLD];
-  __shared__ __attribute__((aligned(16))) half_t Vt[D * VLD];
+  constexpr int DT = D / 16, CB = D / 32, LD = D + 8, TILE = BN * LD;
+  __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
@@ -209,6 +338,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(MfmaParams p) {
   t += t0;
   const int q0 = t * BM, wrow0 = q0 + 32 * w, qrow = wrow0 + l32;
   const size_t head = (size_t)bh * p.N * D;
+  const half_t* kh = p.kh + head;
+  const half_t* vh = p.vh + head;
 
   half8 qf[DT];
   load_frag_rows<D>(qf, p.qh + head, qrow, p.N, g);
@@ -220,52 +351,32 @@ __global__ __launch_bounds__(256) void fwd_kernel(MfmaParams p) {
   const int nk = (p.N + BN - 1) / BN;
   const int n_kt = CAUSAL ? min(nk, (q0 + BM + BN - 1) / BN) : nk;
 
+  TileRegs<D> kr, vr;
+  kr.load(kh, 0, p.N);
+  vr.load(vh, 0, p.N);
+  kr.store(Ks);
+  vr.store(Vs);
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * BN;
-    __syncthreads();
-    stage_rows<D>(Ks, p.kh + head, k0, p.N);
-    stage_rows_t<D>(Vt, p.vh + head, k0, p.N);
-    __syncthreads();
-    if (CAUSAL && k0 > wrow0 + 31) continue;  // whole tile above this wave's rows
-
-    f32x16 s[2];
-    scores<D>(s, Ks, qf, l32, g);
-    const bool need_mask = (CAUSAL && k0 + BN - 1 > wrow0) || (k0 + BN > p.N);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[mb][r] * c2;
-        if (need_mask) {
-          const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= p.N || (CAUSAL && key > qrow)) x = -INFINITY;
-        }
-        s[mb][r] = x;
-        mx = fmaxf(mx, x);
-      }
+    const int cur = (kt & 1) * TILE, nxt = TILE - cur;
+    const bool more = kt + 1 < n_kt;
+    if (more) {
+      kr.load(kh, k0 + BN, p.N);
+      vr.load(vh, k0 + BN, p.N);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float ms = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = exp2_fast(m - ms);
-    float ls = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = exp2_fast(s[mb][r] - ms);
-        s[mb][r] = pr;
-        ls += pr;
-      }
+    if (!(CAUSAL && k0 > wrow0 + 31)) {  // skip tiles wholly above this wave's rows
+      const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;  // last visible key
+      if ((CAUSAL && k0 + BN - 1 > wrow0) || (k0 + BN > p.N))
+        fwd_tile<D, true>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, c2, lane);
+      else
+        fwd_tile<D, false>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, c2, lane);
     }
-    l = l * alpha + ls;
-    m = mn;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
-    half8 pf[4];
-    to_frags(s, pf);
-    accumulate_t<D>(o, Vt, pf, l32, g);
+    if (more) {
+      kr.store(Ks + nxt);
+      vr.store(Vs + nxt);
+    }
+    __syncthreads();
   }
 
   const float lt = l + __shfl_xor(l, 32, 64);
@@ -287,12 +398,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(MfmaParams p) {
 }
 
 // ------------------------------------------------------------------ dQ
+// Workgroup = 128 query rows; streams 64-key tiles of K~ and V.  The K~
+// tile serves both the score product (natural reads) and dQ~ += dS K~
+// (transposed reads).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void dq_kernel(MfmaParams p) {
-  constexpr int DT = D / 16, CB = D / 32, KLD = D + 8, VLD = BN + 8;
-  __shared__ __attribute__((aligned(16))) half_t Ks[BN * KLD];
-  __shared__ __attribute__((aligned(16))) half_t Vs[BN * KLD];
-  __shared__ __attribute__((aligned(16))) half_t Kt[D * VLD];
+  constexpr int DT = D / 16, CB = D / 32, LD = D + 8, TILE = BN * LD;
+  __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
   __shared__ float red[4 * (D / 2)];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
@@ -304,6 +417,8 @@ __global__ __launch_bounds__(256) void dq_kernel(MfmaParams p) {
   t += t0;
   const int q0 = t * BM, wrow0 = q0 + 32 * w, qrow = wrow0 + l32;
   const size_t head = (size_t)bh * p.N * D;
+  const half_t* kh = p.kh + head;
+  const half_t* vh = p.vh + head;
 
   half8 qf[DT], df[DT];
   load_frag_rows<D>(qf, p.qh + head, qrow, p.N, g);
@@ -318,34 +433,32 @@ __global__ __launch_bounds__(256) void dq_kernel(MfmaParams p) {
   const int nk = (p.N + BN - 1) / BN;
   const int n_kt = CAUSAL ? min(nk, (q0 + BM + BN - 1) / BN) : nk;
 
+  TileRegs<D> kr, vr;
+  kr.load(kh, 0, p.N);
+  vr.load(vh, 0, p.N);
+  kr.store(Ks);
+  vr.store(Vs);
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * BN;
-    __syncthreads();
-    stage_rows<D>(Ks, p.kh + head, k0, p.N);
-    stage_rows<D>(Vs, p.vh + head, k0, p.N);
-    stage_rows_t<D>(Kt, p.kh + head, k0, p.N);
-    __syncthreads();
-    if (CAUSAL && k0 > wrow0 + 31) continue;
-
-    f32x16 s[2], dp[2];
-    scores<D>(s, Ks, qf, l32, g);
-    scores<D>(dp, Vs, df, l32, g);
-    const bool need_mask = (CAUSAL && k0 + BN - 1 > wrow0) || (k0 + BN > p.N);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = exp2_fast(s[mb][r] * c2 - lse2);
-        if (need_mask) {
-          const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= p.N || (CAUSAL && key > qrow)) pr = 0.f;
-        }
-        s[mb][r] = pr * (dp[mb][r] - dr);
-      }
+    const int cur = (kt & 1) * TILE, nxt = TILE - cur;
+    const bool more = kt + 1 < n_kt;
+    if (more) {
+      kr.load(kh, k0 + BN, p.N);
+      vr.load(vh, k0 + BN, p.N);
     }
-    half8 sf[4];
-    to_frags(s, sf);
-    accumulate_t<D>(acc, Kt, sf, l32, g);
+    if (!(CAUSAL && k0 > wrow0 + 31)) {
+      const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;
+      if ((CAUSAL && k0 + BN - 1 > wrow0) || (k0 + BN > p.N))
+        dq_tile<D, true>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, c2, lse2, dr, lane);
+      else
+        dq_tile<D, false>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, c2, lse2, dr, lane);
+    }
+    if (more) {
+      kr.store(Ks + nxt);
+      vr.store(Vs + nxt);
+    }
+    __syncthreads();
   }
 
   float wv[D / 4];
@@ -359,27 +472,32 @@ __global__ __launch_bounds__(256) void dq_kernel(MfmaParams p) {
 }
 
 // ------------------------------------------------------------------ dK, dV
+// Workgroup = 128 keys of one head (4 waves x 32 keys); streams 64-row
+// tiles of Q~ and dO (plus their LSE and D values).  Q~ serves the score
+// product and dK~ += dS^T Q~; dO serves dP = dO V^T and dV += P^T dO.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void dkdv_kernel(MfmaParams p) {
-  constexpr int DT = D / 16, CB = D / 32, KLD = D + 8, VLD = BN + 8;
-  __shared__ __attribute__((aligned(16))) half_t Qs[BN * KLD];
-  __shared__ __attribute__((aligned(16))) half_t Ds[BN * KLD];
-  __shared__ __attribute__((aligned(16))) half_t Qt[D * VLD];
-  __shared__ __attribute__((aligned(16))) half_t Dt[D * VLD];
-  __shared__ __attribute__((aligned(16))) float lses[BN];
-  __shared__ __attribute__((aligned(16))) float drs[BN];
+  constexpr int DT = D / 16, CB = D / 32, LD = D + 8, TILE = BN * LD;
+  __shared__ __attribute__((aligned(16))) half_t Qs[2 * TILE];
+  __shared__ __attribute__((aligned(16))) half_t Ds[2 * TILE];
+  __shared__ __attribute__((aligned(16))) float lses[2 * BN];
+  __shared__ __attribute__((aligned(16))) float drs[2 * BN];
   __shared__ float red[4 * (D / 2)];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int ntiles = (p.N + BM - 1) / BM;
   int bh, t;
-  // key tile t has N - 128 t query rows after it under the causal mask:
-  // low tiles are the heavy ones
+  // key tile t has the N - 128 t query rows after it under the causal
+  // mask: low tiles are the heavy ones
   map_block(blockIdx.x, BH, ntiles, false, bh, t);
   const int slot = p.slot0 + blockIdx.x;
   const int k0 = t * BM, wkey0 = k0 + 32 * w, key = wkey0 + l32;
   const size_t head = (size_t)bh * p.N * D;
+  const half_t* qh = p.qh + head;
+  const half_t* doh = p.doh + head;
+  const float* lse_h = p.lse + (size_t)bh * p.N;
+  const float* dr_h = p.drow + (size_t)bh * p.N;
 
   half8 kf[DT], vf[DT];
   load_frag_rows<D>(kf, p.kh + head, key, p.N, g);
@@ -390,52 +508,48 @@ __global__ __launch_bounds__(256) void dkdv_kernel(MfmaParams p) {
   const float c2 = p.scale * LOG2E;
   int qs0 = CAUSAL ? k0 : 0;
   if (qs0 < p.corner) qs0 = p.corner;  // pairs with query rows < corner: exact path
+  const int n_it = qs0 < p.N ? (p.N - qs0 + BN - 1) / BN : 0;
 
-  for (int r0 = qs0; r0 < p.N; r0 += BN) {
-    __syncthreads();
-    stage_rows<D>(Qs, p.qh + head, r0, p.N);
-    stage_rows<D>(Ds, p.doh + head, r0, p.N);
-    stage_rows_t<D>(Qt, p.qh + head, r0, p.N);
-    stage_rows_t<D>(Dt, p.doh + head, r0, p.N);
+  TileRegs<D> qr, dr;
+  float lv = INFINITY, dvv = 0.f;   // row scalars held by threads < BN
+  auto load_rows = [&](int r0) {
+    qr.load(qh, r0, p.N);
+    dr.load(doh, r0, p.N);
     if (threadIdx.x < BN) {
       const int row = r0 + threadIdx.x;
       const bool ok = row < p.N;
-      lses[threadIdx.x] = ok ? p.lse[(size_t)bh * p.N + row] * LOG2E : INFINITY;
-      drs[threadIdx.x] = ok ? p.drow[(size_t)bh * p.N + row] : 0.f;
+      lv = ok ? lse_h[ok ? row : 0] * LOG2E : INFINITY;
+      dvv = ok ? dr_h[ok ? row : 0] : 0.f;
     }
+  };
+  auto store_rows = [&](int buf) {
+    qr.store(Qs + buf * TILE);
+    dr.store(Ds + buf * TILE);
+    if (threadIdx.x < BN) {
+      lses[buf * BN + threadIdx.x] = lv;
+      drs[buf * BN + threadIdx.x] = dvv;
+    }
+  };
+  if (n_it > 0) {
+    load_rows(qs0);
+    store_rows(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    const int r0 = qs0 + it * BN;
+    const int cur = it & 1;
+    const bool more = it + 1 < n_it;
+    if (more) load_rows(r0 + BN);
+    if (!(CAUSAL && wkey0 > r0 + BN - 1)) {  // skip tiles wholly before this wave's keys
+      const half_t* qt = Qs + cur * TILE;
+      const half_t* dt = Ds + cur * TILE;
+      if (CAUSAL && wkey0 + 31 > r0)
+        dkdv_tile<D, true>(dk, dv, qt, dt, lses + cur * BN, drs + cur * BN, kf, vf, r0, key, c2, lane);
+      else
+        dkdv_tile<D, false>(dk, dv, qt, dt, lses + cur * BN, drs + cur * BN, kf, vf, r0, key, c2, lane);
+    }
+    if (more) store_rows(cur ^ 1);
     __syncthreads();
-    if (CAUSAL && wkey0 > r0 + BN - 1) continue;  // all keys of this wave after all rows
-
-    f32x16 s[2], dp[2];
-    scores<D>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
-    scores<D>(dp, Ds, vf, l32, g);
-    const bool need_mask = CAUSAL && wkey0 + 31 > r0;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ql = 32 * mb + 16 * h + 8 * g;
-        const float4 la = *reinterpret_cast<const float4*>(lses + ql);
-        const float4 lb = *reinterpret_cast<const float4*>(lses + ql + 4);
-        const float4 da = *reinterpret_cast<const float4*>(drs + ql);
-        const float4 db = *reinterpret_cast<const float4*>(drs + ql + 4);
-        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-        const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * h + e;
-          float pr = exp2_fast(s[mb][r] * c2 - lv[e]);
-          if (need_mask && key > r0 + ql + e) pr = 0.f;
-          s[mb][r] = pr;
-          dp[mb][r] = pr * (dp[mb][r] - dv8[e]);
-        }
-      }
-    }
-    half8 pf[4], sf[4];
-    to_frags(s, pf);
-    to_frags(dp, sf);
-    accumulate_t<D>(dv, Dt, pf, l32, g);
-    accumulate_t<D>(dk, Qt, sf, l32, g);
   }
 
   float wv[D / 4];

@@ -96,6 +96,40 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
                   int N, int D, int dtype, double base, const float* alpha, int causal,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Staged forms of the two passes, for callers that time or interleave the
+ * phases.  `stages` is a bitwise OR of rope_attn_stage values; calling every
+ * stage in increasing order, on one stream with one workspace and the same
+ * arguments, is exactly rope_attn_fwd / rope_attn_bwd (which call these with
+ * ROPE_ATTN_STAGE_ALL).  A stage reads what the earlier stages left in the
+ * workspace, so the workspace must not be modified in between.
+ *   PREP    frequency table; fp16 operand planes (bf16 inputs); D_i (bwd)
+ *   EXACT   the float32 path: whole problem (fp32 inputs) or the leading
+ *           causal corner, query rows < 128 (bf16 inputs)
+ *   MAIN    forward matrix-core pass (bf16 inputs)
+ *   DQ      dQ matrix-core pass (bf16 inputs)
+ *   DKDV    dK, dV matrix-core pass (bf16 inputs)
+ *   DALPHA  fixed-order reduction of the d alpha partials */
+typedef enum {
+  ROPE_ATTN_STAGE_PREP = 1,
+  ROPE_ATTN_STAGE_EXACT = 2,
+  ROPE_ATTN_STAGE_MAIN = 4,
+  ROPE_ATTN_STAGE_DQ = 8,
+  ROPE_ATTN_STAGE_DKDV = 16,
+  ROPE_ATTN_STAGE_DALPHA = 32,
+  ROPE_ATTN_STAGE_ALL = 63
+} rope_attn_stage;
+
+int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const void* v, float* o,
+                         float* lse, int B, int H, int N, int D, int dtype, double base,
+                         const float* alpha, int causal, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const void* v,
+                         const float* o, const void* dO, const float* lse, float* dq, float* dk,
+                         float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
+                         double base, const float* alpha, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* rope_attn_status_string(int status);
 

@@ -26,8 +26,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["rope_attn_bwd", "rope_attn_bwd_workspace_bytes", "rope_attn_fwd",
-                           "rope_attn_fwd_workspace_bytes", "rope_attn_status_string"]
+    assert _declared() == ["rope_attn_bwd", "rope_attn_bwd_stages", "rope_attn_bwd_workspace_bytes",
+                           "rope_attn_fwd", "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
+                           "rope_attn_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
