@@ -153,6 +153,7 @@ int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const vo
       PrepParams pp = {};
       pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
       pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
+      pp.qscale = LOG2E / sqrtf((float)D);
       launch_prep(pp, hs);
     }
   }
@@ -222,6 +223,7 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
     pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
     pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
+    pp.qscale = LOG2E / sqrtf((float)D);
     launch_prep(pp, hs);
   }
   if ((stages & ROPE_ATTN_STAGE_EXACT) && exact_rows) {

@@ -39,6 +39,7 @@ struct PrepParams {
   const float2* cs;      // [N][D/2]
   half_t* qh; half_t* kh; half_t* vh; half_t* doh;  // fp16 operand planes, any may be null
   float* drow;           // [B,H,N] or null
+  float qscale;          // factor folded into the rotated Q plane
   int bf16;              // input storage: 1 = bf16, 0 = fp32
   int BH, N, D;
 };
@@ -63,6 +64,7 @@ struct SimtParams {
   float scale;
 };
 
+// qh holds Q~ * log2(e) / sqrt(D), so scores come out in log2 units.
 struct MfmaParams {
   const half_t* qh; const half_t* kh; const half_t* vh; const half_t* doh;
   const void* q; const void* k;        // original inputs (for the d alpha wedge)

@@ -60,6 +60,8 @@ __global__ void prep_kernel(PrepParams p) {
       load8(p.q, e0, p.bf16, x);
 #pragma unroll
       for (int i = 0; i < 4; ++i) rot(cs[i].x, cs[i].y, x[2 * i], x[2 * i + 1]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] *= p.qscale;
       store8h(p.qh + e0, x);
     }
     if (p.kh) {
