@@ -21,6 +21,7 @@ import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_TFLOPS = 2516.6   # fp16 / bf16 dense matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
 HBM_GBS = 8000.0
 METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
@@ -40,9 +41,30 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_8k.json"),
+                    help="JSON with measured HBM bytes per launch of the MFMA kernels (used only "
+                         "if it was taken on the current kernel source)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters under rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "bwd_rope_apply_amd", "csrc", "mfma.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(path: str, stage: str):
+    """HBM bytes per launch of `stage` from a counter summary, or None if the
+    summary is missing or was taken on other kernel source."""
+    if not path or not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch", {}).get(stage)
 
 
 def cpu_baseline(inp, wl):
@@ -108,6 +130,13 @@ def main():
     ws_b = torch.empty(_lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal), dtype=torch.uint8, device=dev)
 
     names = [n for n, _ in FWD_STAGES] + [n for n, _ in BWD_STAGES]
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(events=None):
         i = 0
@@ -151,9 +180,7 @@ def main():
     dom = max(STAGE_FLOP_UNITS, key=lambda n: stage_ms[n])
     dom_flops = STAGE_FLOP_UNITS[dom] * unit
     achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(dom)
+    traffic = measured_traffic(args.traffic, dom)
     kernel = {"fwd_main": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}[dom]
     line = {
         "metric": METRIC,

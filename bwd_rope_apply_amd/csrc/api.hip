@@ -19,8 +19,8 @@ struct Shape {
   size_t bh() const { return (size_t)B * H; }
   size_t elems() const { return bh() * N * D; }
   bool bf16() const { return dtype == ROPE_ATTN_BF16; }
-  // exact-corner rows: bf16 causal only
-  int corner() const { return (bf16() && causal) ? CORNER : 0; }
+  // split-operand corner rows: bf16 causal only
+  int corner() const { return (bf16() && causal) ? corner_rows(N) : 0; }
 };
 
 int check_shape(const Shape& s) {
@@ -38,9 +38,11 @@ bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 // Workspace regions, in order.  Sizes are 0 for regions a call does not use.
 struct Layout {
-  size_t theta, cs, qh, kh, vh, doh, drow, dkp, dvp, part;
+  size_t theta, cs, qh, kh, vh, doh, qlo, klo, drow, dkp, dvp, part;
   int slots;
-  size_t total() const { return theta + cs + qh + kh + vh + doh + drow + dkp + dvp + part; }
+  size_t total() const {
+    return theta + cs + qh + kh + vh + doh + qlo + klo + drow + dkp + dvp + part;
+  }
 };
 
 MfmaParams mfma_base(const Shape& s) {
@@ -61,14 +63,14 @@ Layout layout(const Shape& s, bool bwd) {
   if (s.bf16()) {
     L.qh = L.kh = L.vh = h16;
     if (bwd) L.doh = h16;
+    if (s.corner()) L.qlo = L.klo = up(2 * s.bh() * s.corner() * s.D);
   }
   if (bwd) {
     L.drow = up(sizeof(float) * s.bh() * s.N);
-    if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * CORNER * s.D);
+    if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * s.corner() * s.D);
     if (s.bf16()) {
       const MfmaParams m = mfma_base(s);
-      L.slots = (s.corner() ? simt_slots((int)s.bh(), s.corner()) : 0) + dq_mfma_slots(m) +
-                dkdv_mfma_slots(m);
+      L.slots = (s.corner() ? corner_dq_slots(m) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
     } else {
       L.slots = 2 * simt_slots((int)s.bh(), s.N);
     }
@@ -146,30 +148,36 @@ int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const vo
   half_t* qh = c.take<half_t>(L.qh);
   half_t* kh = c.take<half_t>(L.kh);
   half_t* vh = c.take<half_t>(L.vh);
+  c.take<half_t>(L.doh);
+  half_t* qlo = c.take<half_t>(L.qlo);
+  half_t* klo = c.take<half_t>(L.klo);
 
   if (stages & ROPE_ATTN_STAGE_PREP) {
     tables(s, base, alpha, theta, cs, hs);
     if (s.bf16()) {
       PrepParams pp = {};
       pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
+      pp.qlo = qlo; pp.klo = klo; pp.rlo = s.corner();
       pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
       pp.qscale = LOG2E / sqrtf((float)D);
       launch_prep(pp, hs);
     }
   }
+  MfmaParams mp = mfma_base(s);
+  mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.qlo = qlo; mp.klo = klo; mp.o = o; mp.out_lse = lse;
   if (stages & ROPE_ATTN_STAGE_EXACT) {
-    SimtParams sp = {};
-    sp.q = q; sp.k = k; sp.v = v; sp.cs = cs; sp.out_o = o; sp.out_lse = lse;
-    sp.bf16 = s.bf16(); sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
-    sp.scale = 1.0f / sqrtf((float)D);
-    sp.rows = s.bf16() ? s.corner() : N;
-    if (sp.rows) launch_simt_fwd(sp, hs);
+    if (!s.bf16()) {
+      SimtParams sp = {};
+      sp.q = q; sp.k = k; sp.v = v; sp.cs = cs; sp.out_o = o; sp.out_lse = lse;
+      sp.bf16 = 0; sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
+      sp.scale = 1.0f / sqrtf((float)D);
+      sp.rows = N;
+      launch_simt_fwd(sp, hs);
+    } else if (s.corner()) {
+      launch_corner_fwd(mp, hs);
+    }
   }
-  if ((stages & ROPE_ATTN_STAGE_MAIN) && s.bf16()) {
-    MfmaParams mp = mfma_base(s);
-    mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.o = o; mp.out_lse = lse;
-    launch_fwd_mfma(mp, hs);
-  }
+  if ((stages & ROPE_ATTN_STAGE_MAIN) && s.bf16()) launch_fwd_mfma(mp, hs);
   return finish();
 }
 
@@ -203,17 +211,18 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
   half_t* kh = c.take<half_t>(L.kh);
   half_t* vh = c.take<half_t>(L.vh);
   half_t* doh = c.take<half_t>(L.doh);
+  half_t* qlo = c.take<half_t>(L.qlo);
+  half_t* klo = c.take<half_t>(L.klo);
   float* drow = c.take<float>(L.drow);
   float* dkp = c.take<float>(L.dkp);
   float* dvp = c.take<float>(L.dvp);
   float* part = c.take<float>(L.part);
 
-  // d alpha partial slots: [exact dQ rows | exact dK rows | MFMA dQ | MFMA dK]
+  // d alpha partial slots: [exact or corner dQ rows | exact dK rows | MFMA dQ | MFMA dK]
   const int BHi = (int)s.bh();
-  const int exact_rows = s.bf16() ? s.corner() : N;
-  const int n_exact_dq = exact_rows ? simt_slots(BHi, exact_rows) : 0;
-  const int n_exact_dk = s.bf16() ? 0 : simt_slots(BHi, N);
   MfmaParams mp = mfma_base(s);
+  const int n_exact_dq = s.bf16() ? (s.corner() ? corner_dq_slots(mp) : 0) : simt_slots(BHi, N);
+  const int n_exact_dk = s.bf16() ? 0 : simt_slots(BHi, N);
   const int n_dq = s.bf16() ? dq_mfma_slots(mp) : 0;
   const int n_dk = s.bf16() ? dkdv_mfma_slots(mp) : 0;
 
@@ -222,28 +231,32 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
     PrepParams pp = {};
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
     pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
+    pp.qlo = qlo; pp.klo = klo; pp.rlo = s.corner();
     pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
     pp.qscale = LOG2E / sqrtf((float)D);
     launch_prep(pp, hs);
   }
-  if ((stages & ROPE_ATTN_STAGE_EXACT) && exact_rows) {
-    SimtParams sp = {};
-    sp.q = q; sp.k = k; sp.v = v; sp.dO = dO; sp.o = o; sp.lse = lse; sp.drow = drow; sp.cs = cs;
-    sp.dq = dq; sp.dk = dk; sp.dv = dv; sp.dk_part = dkp; sp.dv_part = dvp;
-    sp.dalpha_part = part;
-    sp.bf16 = s.bf16(); sp.BH = BHi; sp.N = N; sp.D = D; sp.causal = causal;
-    sp.scale = 1.0f / sqrtf((float)D);
-    sp.rows = exact_rows;
-    sp.qend = exact_rows < N ? exact_rows : N;
-    sp.final_ = s.bf16() ? 0 : 1;  // bf16: rotated-frame corner partials for the MFMA pass
-    sp.slot0 = 0;
-    launch_simt_dq(sp, hs);
-    sp.slot0 = n_exact_dq;
-    launch_simt_dkdv(sp, hs);
-  }
-  mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.q = q; mp.k = k; mp.cs = cs;
-  mp.lse = lse; mp.drow = drow; mp.dq = dq; mp.dk = dk; mp.dv = dv;
+  mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.qlo = qlo; mp.klo = klo; mp.q = q; mp.k = k;
+  mp.cs = cs; mp.lse = lse; mp.drow = drow; mp.dq = dq; mp.dk = dk; mp.dv = dv;
   mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
+  if (stages & ROPE_ATTN_STAGE_EXACT) {
+    if (!s.bf16()) {
+      SimtParams sp = {};
+      sp.q = q; sp.k = k; sp.v = v; sp.dO = dO; sp.o = o; sp.lse = lse; sp.drow = drow; sp.cs = cs;
+      sp.dq = dq; sp.dk = dk; sp.dv = dv; sp.dalpha_part = part;
+      sp.bf16 = 0; sp.BH = BHi; sp.N = N; sp.D = D; sp.causal = causal;
+      sp.scale = 1.0f / sqrtf((float)D);
+      sp.rows = N; sp.qend = N; sp.final_ = 1;
+      sp.slot0 = 0;
+      launch_simt_dq(sp, hs);
+      sp.slot0 = n_exact_dq;
+      launch_simt_dkdv(sp, hs);
+    } else if (s.corner()) {
+      mp.slot0 = 0;
+      launch_corner_dq(mp, hs);
+      launch_corner_dkdv(mp, hs);  // rotated-frame partials, no d alpha slots
+    }
+  }
   if ((stages & ROPE_ATTN_STAGE_DQ) && s.bf16()) {
     mp.slot0 = n_exact_dq + n_exact_dk;
     launch_dq_mfma(mp, hs);

@@ -14,12 +14,19 @@ typedef __attribute__((ext_vector_type(2))) _Float16 half2v;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-// Query rows [0, CORNER) of every head (and the keys they see under the
-// causal mask) are computed by the exact fp32 path when the inputs are
-// bf16: those rows average few keys, so their outputs and gradients are the
-// largest entries of each tensor and fp16 operand rounding there would
-// dominate the error relative to the tensor's RMS.
-constexpr int CORNER = 128;
+// Causal corner: query rows [0, corner) of every head, and the keys they
+// see, are computed with split fp16 operands (x = hi + lo, three products per
+// contraction, ~22-bit operands) when the inputs are bf16.  Those rows
+// average few keys, so their outputs and gradients are the largest entries
+// of each tensor, and plain fp16 rounding there would dominate the error
+// relative to the tensor's RMS; the effect grows with N (the typical row
+// averages more keys), so the corner grows with it: 128 rows per 8192
+// positions, at least 128.
+constexpr int CORNER_UNIT = 128;
+__host__ __device__ inline int corner_rows(int N) {
+  const int units = (N + 8191) / 8192;
+  return CORNER_UNIT * (units < 1 ? 1 : units);
+}
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -38,6 +45,8 @@ struct PrepParams {
   const float* o;        // [B,H,N,D] forward output (for D = rowsum(dO*O)), or null
   const float2* cs;      // [N][D/2]
   half_t* qh; half_t* kh; half_t* vh; half_t* doh;  // fp16 operand planes, any may be null
+  half_t* qlo; half_t* klo;  // [BH][rlo][D] low parts x - fp16(x) of rows < rlo, or null
+  int rlo;
   float* drow;           // [B,H,N] or null
   float qscale;          // factor folded into the rotated Q plane
   int bf16;              // input storage: 1 = bf16, 0 = fp32
@@ -67,17 +76,18 @@ struct SimtParams {
 // qh holds Q~ * log2(e) / sqrt(D), so scores come out in log2 units.
 struct MfmaParams {
   const half_t* qh; const half_t* kh; const half_t* vh; const half_t* doh;
+  const half_t* qlo; const half_t* klo;   // [BH][corner][D] low parts (corner kernels)
   const void* q; const void* k;        // original inputs (for the d alpha wedge)
   const float2* cs;
   const float* lse; const float* drow;
   float* o; float* out_lse;
   float* dq; float* dk; float* dv;
-  const float* dk_part; const float* dv_part;   // corner partials [BH][corner][D] or null
+  float* dk_part; float* dv_part;   // corner partials [BH][corner][D] or null
   float* dalpha_part;
   int slot0;
   int bf16;
   int B, H, N, D;
-  int corner;      // rows [0, corner) are done by the exact path
+  int corner;      // rows [0, corner) are done by the corner kernels
   int causal;
   float scale;
 };
@@ -101,6 +111,10 @@ void launch_dq_mfma(const MfmaParams& p, hipStream_t s);
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);
 int dq_mfma_slots(const MfmaParams& p);
 int dkdv_mfma_slots(const MfmaParams& p);
+void launch_corner_fwd(const MfmaParams& p, hipStream_t s);
+void launch_corner_dq(const MfmaParams& p, hipStream_t s);
+void launch_corner_dkdv(const MfmaParams& p, hipStream_t s);
+int corner_dq_slots(const MfmaParams& p);
 void launch_dalpha_reduce(const DalphaParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ device helpers

@@ -44,6 +44,14 @@ __device__ __forceinline__ void store8h(half_t* dst, const float* x) {
   *reinterpret_cast<half8*>(dst) = h;
 }
 
+// x - fp16(x), the low part of a split fp16 operand
+__device__ __forceinline__ void store8lo(half_t* dst, const float* x) {
+  half8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (half_t)(x[i] - (float)(half_t)x[i]);
+  *reinterpret_cast<half8*>(dst) = h;
+}
+
 __global__ void prep_kernel(PrepParams p) {
   const int cpr = p.D / 8;                        // chunks per row (8 or 16)
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -63,12 +71,16 @@ __global__ void prep_kernel(PrepParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] *= p.qscale;
       store8h(p.qh + e0, x);
+      if (p.qlo && pos < p.rlo)
+        store8lo(p.qlo + ((size_t)(row / p.N) * p.rlo + pos) * p.D + chunk * 8, x);
     }
     if (p.kh) {
       load8(p.k, e0, p.bf16, x);
 #pragma unroll
       for (int i = 0; i < 4; ++i) rot(cs[i].x, cs[i].y, x[2 * i], x[2 * i + 1]);
       store8h(p.kh + e0, x);
+      if (p.klo && pos < p.rlo)
+        store8lo(p.klo + ((size_t)(row / p.N) * p.rlo + pos) * p.D + chunk * 8, x);
     }
     if (p.vh) {
       load8(p.v, e0, p.bf16, x);

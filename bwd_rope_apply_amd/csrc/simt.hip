@@ -1,8 +1,6 @@
 // Exact fp32 path: plain fused multiply-adds, one row per group of four
 // lanes (each lane owns D/4 consecutive columns, so every rotation pair stays
-// inside one lane).  It serves every call with fp32 inputs, and for bf16
-// inputs the leading causal corner (query rows < CORNER and the keys they
-// see), whose rows are the largest entries of O, dQ, dK and dV.
+// inside one lane).  It serves every call with fp32 inputs.
 //
 // Forward: S = Q~ K~^T / sqrt(D) with the causal mask j <= i, the
 // normalised softmax s(x), O = P V and the row log-sum-exp ("RoPE attention

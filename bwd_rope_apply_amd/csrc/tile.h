@@ -1,0 +1,245 @@
+// Device building blocks shared by the MFMA kernels (gfx950, wave64):
+// fragment layouts, LDS tile layout, score products, transposed reads,
+// epilogues.
+//
+// Fragment convention of v_mfma_f32_32x32x16_f16 (lane l, l32 = l % 32,
+// g = l / 32):  A[m][k]: lane (m, g) holds k = 8g..8g+7 of a 16-wide k step;
+// B[k][n]: lane (n, g) holds the same k; C[m][n]: lane (n, g) holds rows
+// 8(r/4) + 4g + r%4 in register r.  Every score tile is computed transposed
+// (keys along m, queries along n) so all per-query scalars (row max, row
+// sum, LSE, D) live in one lane.  The A rows of the key operand are read in
+// the order perm(m) (bits 2 and 3 swapped), which makes register r of a
+// score block hold key 16(r/8) + 8g + r%8: the 8 keys a lane needs as the
+// B operand of the next product are then contiguous.
+#pragma once
+
+#include "common.h"
+
+namespace ra {
+namespace {
+
+constexpr int BN = 64;     // rows of a streamed tile per loop step (default)
+constexpr int BM = 128;    // stationary rows per workgroup (4 waves x 32)
+
+__device__ __forceinline__ int perm(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// LDS tile layout ([BN][D + 8] fp16): logical row L (bits b5..b0) is stored
+// at physical row sig(L) = (b5 b4 b2 | b1 b0 b3).  With the 16-byte row pad
+// (4 banks), the natural fragment reads (8 lanes on rows perm(l32)) and the
+// transposed reads (16 lanes on 4 rows x 32 bytes) both touch 32 distinct
+// banks, and every read of a lane is one base address plus immediates.
+__device__ __forceinline__ int sig(int L) {
+  return (L & 48) | ((L & 4) << 1) | ((L & 3) << 1) | ((L >> 3) & 1);
+}
+
+__device__ __forceinline__ f32x16 mfma(half8 a, half8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Block index -> (head, tile).  Workgroups are dispatched round-robin over
+// the 8 XCDs; when the head count allows, each XCD gets a fixed set of heads
+// so that their K/V (or Q/dO) tiles stay in that XCD's L2.  Tiles are issued
+// heaviest first (most causal work).
+__device__ __forceinline__ void map_block(int idx, int BH, int ntiles, bool heavy_high, int& bh,
+                                          int& t) {
+  int k;
+  if ((BH & 7) == 0) {
+    const int hpx = BH >> 3;
+    const int x = idx & 7, s = idx >> 3;
+    bh = x * hpx + s % hpx;
+    k = s / hpx;
+  } else {
+    bh = idx % BH;
+    k = idx / BH;
+  }
+  t = heavy_high ? ntiles - 1 - k : k;
+}
+
+// Register copy of one streamed [BN][D] fp16 tile: every thread holds NCH
+// 16-byte chunks (row = chunk / (D/8)).  Rows at or past N are clamped to
+// N - 1: they are masked downstream, so they only need to be finite.
+template <int D, int ROWS = BN>
+struct TileRegs {
+  static constexpr int CPR = D / 8;
+  static constexpr int NCH = ROWS * CPR / 256;
+  half8 x[NCH];
+  __device__ __forceinline__ void load(const half_t* src, int r0, int N) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + 256 * i;
+      const int row = min(r0 + ch / CPR, N - 1);
+      x[i] = *reinterpret_cast<const half8*>(src + (size_t)row * D + (ch % CPR) * 8);
+    }
+  }
+  __device__ __forceinline__ void store(half_t* dst) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + 256 * i;
+      *reinterpret_cast<half8*>(dst + sig(ch / CPR) * (D + 8) + (ch % CPR) * 8) = x[i];
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void load_frag_rows(half8* f, const half_t* src, int row, int N, int g) {
+  // B-operand fragment of one row: k steps t -> columns 16t + 8g .. +8
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    half8 x = {};
+    if (row < N) x = *reinterpret_cast<const half8*>(src + (size_t)row * D + 16 * t + 8 * g);
+    f[t] = x;
+  }
+}
+
+// Two 32-key score blocks (keys along m, this lane's query along n), the
+// accumulators seeded with `seed` (a per-query offset folded into the product).
+template <int D, int NMB = 2>
+__device__ __forceinline__ void scores(f32x16* s, const half_t* lds, const half8* bf, int l32,
+                                       int g, float seed = 0.f) {
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = seed;
+    const half_t* row = lds + sig(32 * mb + perm(l32)) * (D + 8) + 8 * g;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc = mfma(*reinterpret_cast<const half8*>(row + 16 * t), bf[t], acc);
+    s[mb] = acc;
+  }
+}
+
+// s[mb] += the same products (for split-operand sums).
+template <int D, int NMB = 2>
+__device__ __forceinline__ void scores_add(f32x16* s, const half_t* lds, const half8* bf, int l32,
+                                           int g) {
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const half_t* row = lds + sig(32 * mb + perm(l32)) * (D + 8) + 8 * g;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) s[mb] = mfma(*reinterpret_cast<const half8*>(row + 16 * t), bf[t], s[mb]);
+  }
+}
+
+// Split-fp16 fragments: hi = fp16(x), lo = fp16(x - hi).
+template <int NMB = 2>
+__device__ __forceinline__ void to_frags_split(const f32x16* s, half8* hi, half8* lo) {
+#pragma unroll
+  for (int t = 0; t < 2 * NMB; ++t) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = s[t >> 1][8 * (t & 1) + e];
+      const half_t h = (half_t)x;
+      hi[t][e] = h;
+      lo[t][e] = (half_t)(x - (float)h);
+    }
+  }
+}
+
+// Pack register values of NMB score blocks into the 2 NMB 16-key B-operand
+// fragments (k step t holds keys 16t + 8g + e).
+template <int NMB = 2>
+__device__ __forceinline__ void to_frags(const f32x16* s, half8* f) {
+#pragma unroll
+  for (int t = 0; t < 2 * NMB; ++t) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[t][e] = (half_t)s[t >> 1][8 * (t & 1) + e];
+  }
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ s16x4 ds_read_tr(const half_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// A-operand fragment of X^T for k step t and column block cb, X a [BN][D]
+// tile in LDS (two transposed reads).
+template <int D>
+__device__ __forceinline__ half8 tr_frag(const half_t* lds, int t, int cb, int lane) {
+  // logical rows 16t + 8g + 4h + e, e = s16 >> 2 (h = 0, 1), columns
+  // 32cb + 16 b + 4 (s16 & 3): physical row 16t + 8h + sig(8g + e)
+  constexpr int LD = D + 8;
+  const int s16 = lane & 15, g = lane >> 5, b = (lane >> 4) & 1;
+  const half_t* p = lds + (sig(8 * g + (s16 >> 2)) + 16 * t) * LD + 32 * cb + 16 * b + 4 * (s16 & 3);
+  const s16x4 lo = ds_read_tr(p), hi = ds_read_tr(p + 8 * LD);
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(half8, both);
+}
+
+// acc[cb] += X^T(columns 32cb.., rows = 16-wide k steps) * frag, with X a
+// [BN][D + 8] tile in LDS.  ds_read_b64_tr_b16 transposes a 4 x 16 block per
+// 16-lane group (lane j receives element j of the 4 rows that lanes
+// 4e + j/4 point at), so lane s of a group points at row s/4, columns
+// 4 (s % 4) .. +3 of its block, and two reads give the 8 k-values (rows
+// 16t + 8g + 0..7) of column 32cb + l32.
+template <int D, int NT = 4>
+__device__ __forceinline__ void accumulate_tr(f32x16* acc, const half_t* lds, const half8* f, int lane) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[cb] = mfma(tr_frag<D>(lds, t, cb, lane), f[t], acc[cb]);
+  }
+}
+
+// Position-weighted wedge partial of one row's gradient (already in the
+// un-rotated frame) summed over the workgroup into one [D/2] slot.
+// w[cb*8 + rq*2 + h] is pair m = 16cb + 4rq + 2g + h.
+template <int D>
+__device__ __forceinline__ void store_dalpha(float* w, float* red, float* slot, int g) {
+  constexpr int NW = D / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    float x = w[i];
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    x += __shfl_xor(x, 16, 64);
+    if ((lane & 31) == 0) {
+      const int cb = i >> 3, rq = (i >> 1) & 3, h = i & 1;
+      red[wave * (D / 2) + 16 * cb + 4 * rq + 2 * g + h] = x;
+    }
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m < D / 2; m += 256)
+    slot[m] = (red[m] + red[D / 2 + m]) + (red[D + m] + red[3 * D / 2 + m]);
+}
+
+// Un-rotate one lane's gradient registers (row `row`, columns
+// 32cb + 8rq + 4g + 0..3), add the wedge partials and store float4s.
+template <int D>
+__device__ __forceinline__ void finish_rows(f32x16* acc, float scale, const float* part_row,
+                                            const float2* cs_row, const void* x_in, size_t x_off,
+                                            int bf16, float* out, float pos, float* w, int g) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int c = 32 * cb + 8 * rq + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * rq + e] * scale;
+      if (part_row) {
+        const float4 pr = *reinterpret_cast<const float4*>(part_row + c);
+        v[0] += pr.x; v[1] += pr.y; v[2] += pr.z; v[3] += pr.w;
+      }
+      const float2 t0 = cs_row[c / 2], t1 = cs_row[c / 2 + 1];
+      unrot(t0.x, t0.y, v[0], v[1]);
+      unrot(t1.x, t1.y, v[2], v[3]);
+      float x[4];
+      load4(x_in, x_off + c, bf16, x);
+      w[cb * 8 + rq * 2 + 0] = pos * (x[0] * v[1] - x[1] * v[0]);
+      w[cb * 8 + rq * 2 + 1] = pos * (x[2] * v[3] - x[3] * v[2]);
+      *reinterpret_cast<float4*>(out + c) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace ra

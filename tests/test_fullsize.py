@@ -1,0 +1,75 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.
+
+The whole problem runs on the GPU.  The float64 oracle then evaluates two
+complete heads (the first and the last) and every output of those heads is
+compared under the bf16 bar (max |err| / rms(ref) <= 2e-2, RMS pooled over
+the two heads).  dalpha sums over every head: where the oracle finishes all
+heads in seconds it is compared directly; otherwise the GPU's dalpha is
+checked against theta_hat_m * sum_p p * wedge(x_p, g_p) evaluated from the
+GPU's own dQ, dK (a property that holds at any size).  Rotational balance
+holds per (b, h, m) for every head.
+"""
+import numpy as np
+import pytest
+
+from bwd_rope_apply_amd import workloads as W
+import harness as Hn
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _wedge(x, g):
+    return x[..., 0::2] * g[..., 1::2] - x[..., 1::2] * g[..., 0::2]
+
+
+@pytest.mark.parametrize("name,all_heads_dalpha", [
+    ("layer_2k", True), ("long_8k", True), ("train_4k", False), ("vlong_32k", False)])
+def test_full_size(name, all_heads_dalpha):
+    from oracle import ref
+    wl = W.get(name)
+    inp = W.make_inputs(wl)
+    print(f"{name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D}", flush=True)
+    got = Hn.run_gpu(inp)
+    for n in ("O", "LSE", "dQ", "dK", "dV", "dalpha"):
+        assert np.isfinite(got[n]).all(), n
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    refs = {n: [] for n in ("O", "dQ", "dK", "dV")}
+    gots = {n: [] for n in refs}
+    lse_err = 0.0
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o, lse = ref.ref_fwd(q[sl], k[sl], v[sl], wl.base, inp.alpha, wl.causal)
+        dq, dk, dv, _ = ref.ref_bwd(q[sl], k[sl], v[sl], o, do[sl], lse, wl.base, inp.alpha, wl.causal)
+        for n, r in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+            refs[n].append(r[0, 0])
+            gots[n].append(got[n][b, h])
+        lse_err = max(lse_err, float(np.abs(got["LSE"][b, h] - lse[0, 0]).max()))
+    errs = {n: Hn.err_rms(np.stack(gots[n]), np.stack(refs[n])) for n in refs}
+    errs["LSE_abs"] = lse_err
+    print(name, errs, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)
+
+    # rotational balance on every head
+    wq = _wedge(q, got["dQ"]).sum(axis=2)
+    wk = _wedge(k, got["dK"]).sum(axis=2)
+    scale = np.abs(_wedge(q, got["dQ"])).sum(axis=2).max()
+    assert np.abs(wq + wk).max() <= 1e-3 * scale
+
+    th = ref.theta_hat(wl.base, inp.alpha, wl.D)
+    if all_heads_dalpha:
+        o, lse = ref.ref_fwd(q, k, v, wl.base, inp.alpha, wl.causal)
+        want = ref.ref_bwd(q, k, v, o, do, lse, wl.base, inp.alpha, wl.causal)[3]
+        e = Hn.err_rms(got["dalpha"], want)
+        print(name, "dalpha vs oracle (all heads):", e, flush=True)
+        assert e <= TOL
+    else:
+        pos = np.arange(wl.N, dtype=np.float64)[:, None]
+        prop = th * ((pos * _wedge(q, got["dQ"])).sum(axis=(0, 1, 2)) +
+                     (pos * _wedge(k, got["dK"])).sum(axis=(0, 1, 2)))
+        e = Hn.err_rms(got["dalpha"], prop)
+        print(name, "dalpha vs its definition on the GPU's dQ, dK:", e, flush=True)
+        assert e <= 1e-3
