@@ -253,32 +253,31 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
   const int n_kt = CAUSAL ? min(nk, (q0 + FWD_BM + BN - 1) / BN) : nk;
   const int wlast = wrow0 + 32 * NB - 1;
 
-  TileRegs<D> kr, vr;
-  kr.load(kh, 0, p.N);
-  vr.load(vh, 0, p.N);
-  kr.store(Ks);
-  vr.store(Vs);
+  TileDMA<D, BN> dma;
+  dma.init(lane, w);
+  dma.load(Ks, kh, 0, p.N, w);
+  dma.load(Vs, vh, 0, p.N, w);
+  wait_lds_copies();
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // steps before `split` need no mask for any wave (the workgroup's diagonal
+  // and the ragged tail come after); the loop is peeled there so each loop
+  // carries a single inlined tile body
+  const int split = min(n_kt, min(CAUSAL ? q0 / BN : nk, p.N / BN));
+  auto step = [&](int kt, auto masked) {
     const int k0 = kt * BN;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
-    const bool more = kt + 1 < n_kt;
-    if (more) {
-      kr.load(kh, k0 + BN, p.N);
-      vr.load(vh, k0 + BN, p.N);
+    if (kt + 1 < n_kt) {
+      dma.load(Ks + nxt, kh, k0 + BN, p.N, w);
+      dma.load(Vs + nxt, vh, k0 + BN, p.N, w);
     }
-    if (active && !(CAUSAL && k0 > wlast)) {  // skip tiles wholly above this wave's rows
-      if ((CAUSAL && k0 + BN - 1 > wrow0) || (k0 + BN > p.N))
-        fwd_tile<D, NB, true>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, lane);
-      else
-        fwd_tile<D, NB, false>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, lane);
-    }
-    if (more) {
-      kr.store(Ks + nxt);
-      vr.store(Vs + nxt);
-    }
+    if (active && !(CAUSAL && k0 > wlast))  // skip tiles wholly above this wave's rows
+      fwd_tile<D, NB, decltype(masked)::value>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, lane);
+    wait_lds_copies();
     __syncthreads();
-  }
+  };
+  int kt = 0;
+  for (; kt < split; ++kt) step(kt, std::false_type{});
+  for (; kt < n_kt; ++kt) step(kt, std::true_type{});
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -338,33 +337,32 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
   const int nk = (p.N + KB - 1) / KB;
   const int n_kt = CAUSAL ? min(nk, (q0 + BM + KB - 1) / KB) : nk;
 
-  TileRegs<D, KB> kr, vr;
-  kr.load(kh, 0, p.N);
-  vr.load(vh, 0, p.N);
-  kr.store(Ks);
-  vr.store(Vs);
+  TileDMA<D, KB> dma;
+  dma.init(lane, w);
+  dma.load(Ks, kh, 0, p.N, w);
+  dma.load(Vs, vh, 0, p.N, w);
+  wait_lds_copies();
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;
+  // unmasked steps first, then the diagonal and ragged tail (peeled loops,
+  // one inlined tile body each)
+  const int split = min(n_kt, min(CAUSAL ? q0 / KB : nk, p.N / KB));
+  auto step = [&](int kt, auto masked) {
     const int k0 = kt * KB;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
-    const bool more = kt + 1 < n_kt;
-    if (more) {
-      kr.load(kh, k0 + KB, p.N);
-      vr.load(vh, k0 + KB, p.N);
+    if (kt + 1 < n_kt) {
+      dma.load(Ks + nxt, kh, k0 + KB, p.N, w);
+      dma.load(Vs + nxt, vh, k0 + KB, p.N, w);
     }
-    if (!(CAUSAL && k0 > wrow0 + 31)) {
-      const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;
-      if ((CAUSAL && k0 + KB - 1 > wrow0) || (k0 + KB > p.N))
-        dq_tile<D, NMB, true>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, lse2, dr, lane);
-      else
-        dq_tile<D, NMB, false>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, lse2, dr, lane);
-    }
-    if (more) {
-      kr.store(Ks + nxt);
-      vr.store(Vs + nxt);
-    }
+    if (!(CAUSAL && k0 > wrow0 + 31))
+      dq_tile<D, NMB, decltype(masked)::value>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, lse2, dr,
+                                               lane);
+    wait_lds_copies();
     __syncthreads();
-  }
+  };
+  int kt = 0;
+  for (; kt < split; ++kt) step(kt, std::false_type{});
+  for (; kt < n_kt; ++kt) step(kt, std::true_type{});
 
   float wv[D / 4];
 #pragma unroll
@@ -415,11 +413,12 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   if (qs0 < p.corner) qs0 = p.corner;  // pairs with query rows < corner: exact path
   const int n_it = qs0 < p.N ? (p.N - qs0 + QB - 1) / QB : 0;
 
-  TileRegs<D, QB> qr, dr;
+  TileDMA<D, QB> dma;
+  dma.init(lane, w);
   float lv = INFINITY, dvv = 0.f;   // row scalars held by threads < QB
-  auto load_rows = [&](int r0) {
-    qr.load(qh, r0, p.N);
-    dr.load(doh, r0, p.N);
+  auto load_rows = [&](int r0, int buf) {
+    dma.load(Qs + buf * TILE, qh, r0, p.N, w);
+    dma.load(Ds + buf * TILE, doh, r0, p.N, w);
     if (threadIdx.x < QB) {
       const int row = r0 + threadIdx.x;
       const bool ok = row < p.N;
@@ -428,34 +427,36 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     }
   };
   auto store_rows = [&](int buf) {
-    qr.store(Qs + buf * TILE);
-    dr.store(Ds + buf * TILE);
     if (threadIdx.x < QB) {
       lses[buf * QB + threadIdx.x] = lv;
       drs[buf * QB + threadIdx.x] = dvv;
     }
   };
   if (n_it > 0) {
-    load_rows(qs0);
+    load_rows(qs0, 0);
     store_rows(0);
   }
+  wait_lds_copies();
   __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
+  // the first steps cross the workgroup's diagonal (masked), the rest need
+  // no mask: peeled loops, one inlined tile body each
+  const int n_masked = (CAUSAL && qs0 <= k0 + BM - 2) ? min(n_it, (k0 + BM - 2 - qs0) / QB + 1) : 0;
+  auto step = [&](int it, auto masked) {
     const int r0 = qs0 + it * QB;
     const int cur = it & 1;
     const bool more = it + 1 < n_it;
-    if (more) load_rows(r0 + QB);
-    if (!(CAUSAL && wkey0 > r0 + QB - 1)) {  // skip tiles wholly before this wave's keys
-      const half_t* qt = Qs + cur * TILE;
-      const half_t* dt = Ds + cur * TILE;
-      if (CAUSAL && wkey0 + 31 > r0)
-        dkdv_tile<D, NMB, true>(dk, dv, qt, dt, lses + cur * QB, drs + cur * QB, kf, vf, r0, key, lane);
-      else
-        dkdv_tile<D, NMB, false>(dk, dv, qt, dt, lses + cur * QB, drs + cur * QB, kf, vf, r0, key, lane);
-    }
+    if (more) load_rows(r0 + QB, cur ^ 1);
+    if (!(CAUSAL && wkey0 > r0 + QB - 1))  // skip tiles wholly before this wave's keys
+      dkdv_tile<D, NMB, decltype(masked)::value>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
+                                                 lses + cur * QB, drs + cur * QB, kf, vf, r0, key,
+                                                 lane);
     if (more) store_rows(cur ^ 1);
+    wait_lds_copies();
     __syncthreads();
-  }
+  };
+  int it = 0;
+  for (; it < n_masked; ++it) step(it, std::true_type{});
+  for (; it < n_it; ++it) step(it, std::false_type{});
 
   float wv[D / 4];
 #pragma unroll

@@ -13,6 +13,8 @@
 // B operand of the next product are then contiguous.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace ra {
@@ -83,6 +85,50 @@ struct TileRegs {
     }
   }
 };
+
+__device__ __forceinline__ int sig_inv(int P) {
+  return (P & 48) | ((P & 1) << 3) | ((P >> 1) & 7);
+}
+
+// Direct global -> LDS copy of one streamed [ROWS][D] fp16 tile into the
+// sig() layout, without passing through registers (global_load_lds_dwordx4:
+// each wave instruction writes 1 KiB of LDS, lane i at byte 16 i).  The tile
+// is covered by consecutive 1 KiB blocks, block b issued by wave b % 4; a
+// lane whose 16-byte slot falls in a row pad loads a dummy chunk.  Rows at or
+// past N are clamped to N - 1 (masked downstream).  Callers wait for the
+// copies (wait_lds_copies) before the barrier that publishes the tile.
+template <int D, int ROWS>
+struct TileDMA {
+  static constexpr int RB = (D + 8) * 2;                 // bytes per physical row
+  static constexpr int BYTES = ROWS * RB;
+  static constexpr int NBLK = (BYTES + 1023) / 1024;
+  static constexpr int PER_WAVE = (NBLK + 3) / 4;
+  int lc[PER_WAVE];   // logical row * 64 + chunk; -1 row pad; -2 past the tile
+  __device__ __forceinline__ void init(int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int o = (wave + 4 * i) * 1024 + 16 * lane;
+      const int pr = o / RB, within = o % RB;
+      lc[i] = (o >= BYTES) ? -2 : (within >= 2 * D ? -1 : sig_inv(pr) * 64 + within / 16);
+    }
+  }
+  __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0, int N,
+                                       int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int b = wave + 4 * i;
+      if (b < NBLK && lc[i] != -2) {
+        const int v = lc[i] < 0 ? 0 : lc[i];
+        const int row = min(r0 + (v >> 6), N - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src + (size_t)row * D + (v & 63) * 8),
+            (__attribute__((address_space(3))) void*)(tile + b * 512), 16, 0, 0);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0); }
 
 template <int D>
 __device__ __forceinline__ void load_frag_rows(half8* f, const half_t* src, int row, int N, int g) {
