@@ -33,16 +33,19 @@ namespace {
 #define RA_FWD_SEED 0      // 1: fold the running max into the score accumulators
 #endif
 #ifndef RA_DQ_BN
-#define RA_DQ_BN 64
+#define RA_DQ_BN 32
 #endif
 #ifndef RA_DQ_WPS
-#define RA_DQ_WPS 1
+#define RA_DQ_WPS 2
 #endif
 #ifndef RA_DKDV_BN
-#define RA_DKDV_BN 64
+#define RA_DKDV_BN 32
 #endif
 #ifndef RA_DKDV_WPS
-#define RA_DKDV_WPS 1
+#define RA_DKDV_WPS 2
+#endif
+#ifndef RA_DKDV_VLDS
+#define RA_DKDV_VLDS 1     // 1: keep the stationary V tile in LDS instead of registers
 #endif
 
 
@@ -174,12 +177,19 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const hal
 template <int D, int NMB, bool MASK>
 __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* Qs,
                                           const half_t* Ds, const float* lses, const float* drs,
-                                          const half8* kf, const half8* vf, int r0, int key,
-                                          int lane) {
+                                          const half8* kf, const half8* vf, const half_t* vrow,
+                                          int r0, int key, int lane) {
   const int l32 = lane & 31, g = lane >> 5;
   f32x16 s[NMB], dp[NMB];
   scores<D, NMB>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
-  scores<D, NMB>(dp, Ds, vf, l32, g);
+  if (vrow) {  // V fragments of this lane's key read from the stationary LDS tile
+    half8 vl[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) vl[t] = *reinterpret_cast<const half8*>(vrow + 16 * t);
+    scores<D, NMB>(dp, Ds, vl, l32, g);
+  } else {
+    scores<D, NMB>(dp, Ds, vf, l32, g);
+  }
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -384,6 +394,7 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   constexpr int DT = D / 16, CB = D / 32, TILE = QB * (D + 8);
   __shared__ __attribute__((aligned(16))) half_t Qs[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Ds[2 * TILE];
+  __shared__ __attribute__((aligned(16))) half_t Vst[RA_DKDV_VLDS ? BM * (D + 8) : 8];
   __shared__ __attribute__((aligned(16))) float lses[2 * QB];
   __shared__ __attribute__((aligned(16))) float drs[2 * QB];
   __shared__ float red[4 * (D / 2)];
@@ -403,9 +414,21 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   const float* lse_h = p.lse + (size_t)bh * p.N;
   const float* dr_h = p.drow + (size_t)bh * p.N;
 
-  half8 kf[DT], vf[DT];
+  half8 kf[DT], vf[RA_DKDV_VLDS ? 1 : DT];
   load_frag_rows<D>(kf, p.kh + head, key, p.N, g);
-  load_frag_rows<D>(vf, p.vh + head, key, p.N, g);
+  const half_t* vrow = nullptr;
+  if (RA_DKDV_VLDS) {
+    // rows k0 .. k0 + 127 of V, padded rows; lane reads row 32 w + l32
+    for (int ch = threadIdx.x; ch < BM * (D / 8); ch += 256) {
+      const int r = ch / (D / 8), c8 = ch % (D / 8);
+      const int row = min(k0 + r, p.N - 1);
+      *reinterpret_cast<half8*>(Vst + r * (D + 8) + c8 * 8) =
+          *reinterpret_cast<const half8*>(p.vh + head + (size_t)row * D + c8 * 8);
+    }
+    vrow = Vst + (32 * w + l32) * (D + 8) + 8 * g;
+  } else {
+    load_frag_rows<D>(vf, p.vh + head, key, p.N, g);
+  }
   f32x16 dk[CB], dv[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) { dk[cb] = f32x16{}; dv[cb] = f32x16{}; }
@@ -448,8 +471,8 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     if (more) load_rows(r0 + QB, cur ^ 1);
     if (!(CAUSAL && wkey0 > r0 + QB - 1))  // skip tiles wholly before this wave's keys
       dkdv_tile<D, NMB, decltype(masked)::value>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
-                                                 lses + cur * QB, drs + cur * QB, kf, vf, r0, key,
-                                                 lane);
+                                                 lses + cur * QB, drs + cur * QB, kf, vf, vrow, r0,
+                                                 key, lane);
     if (more) store_rows(cur ^ 1);
     wait_lds_copies();
     __syncthreads();
