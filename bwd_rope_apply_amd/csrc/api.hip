@@ -38,10 +38,10 @@ bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 // Workspace regions, in order.  Sizes are 0 for regions a call does not use.
 struct Layout {
-  size_t theta, cs, qh, kh, vh, doh, qlo, klo, drow, dkp, dvp, part;
+  size_t theta, cs, qh, kh, vh, doh, qlo, klo, drow, rs, dkp, dvp, part;
   int slots;
   size_t total() const {
-    return theta + cs + qh + kh + vh + doh + qlo + klo + drow + dkp + dvp + part;
+    return theta + cs + qh + kh + vh + doh + qlo + klo + drow + rs + dkp + dvp + part;
   }
 };
 
@@ -67,6 +67,7 @@ Layout layout(const Shape& s, bool bwd) {
   }
   if (bwd) {
     L.drow = up(sizeof(float) * s.bh() * s.N);
+    if (s.bf16()) L.rs = up(sizeof(float) * s.bh() * rs_groups(s.N) * 64);
     if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * s.corner() * s.D);
     if (s.bf16()) {
       const MfmaParams m = mfma_base(s);
@@ -214,6 +215,7 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
   half_t* qlo = c.take<half_t>(L.qlo);
   half_t* klo = c.take<half_t>(L.klo);
   float* drow = c.take<float>(L.drow);
+  float* rs = c.take<float>(L.rs);
   float* dkp = c.take<float>(L.dkp);
   float* dvp = c.take<float>(L.dvp);
   float* part = c.take<float>(L.part);
@@ -231,13 +233,14 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
     PrepParams pp = {};
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
     pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
+    pp.lse = lse; pp.rs = rs;
     pp.qlo = qlo; pp.klo = klo; pp.rlo = s.corner();
     pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
     pp.qscale = LOG2E / sqrtf((float)D);
     launch_prep(pp, hs);
   }
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.qlo = qlo; mp.klo = klo; mp.q = q; mp.k = k;
-  mp.cs = cs; mp.lse = lse; mp.drow = drow; mp.dq = dq; mp.dk = dk; mp.dv = dv;
+  mp.cs = cs; mp.lse = lse; mp.drow = drow; mp.rs = rs; mp.dq = dq; mp.dk = dk; mp.dv = dv;
   mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
   if (stages & ROPE_ATTN_STAGE_EXACT) {
     if (!s.bf16()) {

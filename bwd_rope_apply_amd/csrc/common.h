@@ -28,6 +28,11 @@ __host__ __device__ inline int corner_rows(int N) {
   return CORNER_UNIT * (units < 1 ? 1 : units);
 }
 
+// Backward row scalars in 32-row groups: [LSE * log2(e) x 32 | D x 32] per
+// group, one spare group after the last; rows >= N hold (+inf, 0) so that
+// their P = exp2(S - LSE2) is exactly 0.
+__host__ __device__ inline int rs_groups(int N) { return (N + 31) / 32 + 1; }
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -48,6 +53,8 @@ struct PrepParams {
   half_t* qlo; half_t* klo;  // [BH][rlo][D] low parts x - fp16(x) of rows < rlo, or null
   int rlo;
   float* drow;           // [B,H,N] or null
+  const float* lse;      // [B,H,N] forward LSE (natural log), with rs
+  float* rs;             // [BH][rs_groups(N)][64] row scalars, or null
   float qscale;          // factor folded into the rotated Q plane
   int bf16;              // input storage: 1 = bf16, 0 = fp32
   int BH, N, D;
@@ -80,6 +87,7 @@ struct MfmaParams {
   const void* q; const void* k;        // original inputs (for the d alpha wedge)
   const float2* cs;
   const float* lse; const float* drow;
+  const float* rs;                     // [BH][rs_groups(N)][64] row scalars (dK/dV)
   float* o; float* out_lse;
   float* dq; float* dk; float* dv;
   float* dk_part; float* dv_part;   // corner partials [BH][corner][D] or null

@@ -44,9 +44,6 @@ namespace {
 #ifndef RA_DKDV_WPS
 #define RA_DKDV_WPS 2
 #endif
-#ifndef RA_DKDV_VLDS
-#define RA_DKDV_VLDS 1     // 1: keep the stationary V tile in LDS instead of registers
-#endif
 
 
 // One 64-key step of the forward for one wave owning NB blocks of 32 query
@@ -173,32 +170,32 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const hal
 
 // One step of dK, dV for one wave over 32 NMB queries (this lane's key
 // along n): P = exp(S - LSE), dV += P^T dO, dP = dO V^T, dS = P o (dP - D),
-// dK~ += dS^T Q~.  MASK hides queries before this lane's key.
+// dK~ += dS^T Q~.  MASK hides queries before this lane's key.  rsc holds
+// the step's row scalars, 32-row groups of [LSE * log2(e) | D]; vrow points
+// at this lane's V row in the stationary LDS tile.
 template <int D, int NMB, bool MASK>
 __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* Qs,
-                                          const half_t* Ds, const float* lses, const float* drs,
-                                          const half8* kf, const half8* vf, const half_t* vrow,
-                                          int r0, int key, int lane) {
+                                          const half_t* Ds, const float* rsc, const half8* kf,
+                                          const half_t* vrow, int r0, int key, int lane) {
   const int l32 = lane & 31, g = lane >> 5;
   f32x16 s[NMB], dp[NMB];
   scores<D, NMB>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
-  if (vrow) {  // V fragments of this lane's key read from the stationary LDS tile
+  {
     half8 vl[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) vl[t] = *reinterpret_cast<const half8*>(vrow + 16 * t);
     scores<D, NMB>(dp, Ds, vl, l32, g);
-  } else {
-    scores<D, NMB>(dp, Ds, vf, l32, g);
   }
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int ql = 32 * mb + 16 * h + 8 * g;
-      const float4 la = *reinterpret_cast<const float4*>(lses + ql);
-      const float4 lb = *reinterpret_cast<const float4*>(lses + ql + 4);
-      const float4 da = *reinterpret_cast<const float4*>(drs + ql);
-      const float4 db = *reinterpret_cast<const float4*>(drs + ql + 4);
+      const float* lr = rsc + 64 * mb + 16 * h + 8 * g;
+      const float4 la = *reinterpret_cast<const float4*>(lr);
+      const float4 lb = *reinterpret_cast<const float4*>(lr + 4);
+      const float4 da = *reinterpret_cast<const float4*>(lr + 32);
+      const float4 db = *reinterpret_cast<const float4*>(lr + 36);
       const float lv8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
       const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
@@ -228,7 +225,7 @@ constexpr int FWD_BM = 4 * 32 * FWD_NB;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
-  constexpr int DT = D / 16, CB = D / 32, TILE = BN * (D + 8), NB = FWD_NB;
+  constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, BN>::ALLOC, NB = FWD_NB;
   __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
 
@@ -265,8 +262,8 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
 
   TileDMA<D, BN> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, 0, p.N, w);
-  dma.load(Vs, vh, 0, p.N, w);
+  dma.load(Ks, kh, 0, p.N);
+  dma.load(Vs, vh, 0, p.N);
   wait_lds_copies();
   __syncthreads();
   // steps before `split` need no mask for any wave (the workgroup's diagonal
@@ -277,9 +274,10 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
     const int k0 = kt * BN;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
     if (kt + 1 < n_kt) {
-      dma.load(Ks + nxt, kh, k0 + BN, p.N, w);
-      dma.load(Vs + nxt, vh, k0 + BN, p.N, w);
+      dma.load(Ks + nxt, kh, k0 + BN, p.N);
+      dma.load(Vs + nxt, vh, k0 + BN, p.N);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (active && !(CAUSAL && k0 > wlast))  // skip tiles wholly above this wave's rows
       fwd_tile<D, NB, decltype(masked)::value>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, lane);
     wait_lds_copies();
@@ -318,7 +316,7 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
   constexpr int KB = RA_DQ_BN, NMB = KB / 32;
-  constexpr int DT = D / 16, CB = D / 32, TILE = KB * (D + 8);
+  constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, KB>::ALLOC;
   __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
   __shared__ float red[4 * (D / 2)];
@@ -349,8 +347,8 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
 
   TileDMA<D, KB> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, 0, p.N, w);
-  dma.load(Vs, vh, 0, p.N, w);
+  dma.load(Ks, kh, 0, p.N);
+  dma.load(Vs, vh, 0, p.N);
   wait_lds_copies();
   __syncthreads();
   const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;
@@ -361,9 +359,10 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
     const int k0 = kt * KB;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
     if (kt + 1 < n_kt) {
-      dma.load(Ks + nxt, kh, k0 + KB, p.N, w);
-      dma.load(Vs + nxt, vh, k0 + KB, p.N, w);
+      dma.load(Ks + nxt, kh, k0 + KB, p.N);
+      dma.load(Vs + nxt, vh, k0 + KB, p.N);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (!(CAUSAL && k0 > wrow0 + 31))
       dq_tile<D, NMB, decltype(masked)::value>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, lse2, dr,
                                                lane);
@@ -386,17 +385,17 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
 
 // ------------------------------------------------------------------ dK, dV
 // Workgroup = 128 keys of one head (4 waves x 32 keys); streams QB-row
-// tiles of Q~ and dO (plus their LSE and D values).  Q~ serves the score
-// product and dK~ += dS^T Q~; dO serves dP = dO V^T and dV += P^T dO.
+// tiles of Q~ and dO plus their row scalars.  Q~ serves the score product
+// and dK~ += dS^T Q~; dO serves dP = dO V^T and dV += P^T dO.  The
+// workgroup's V rows stay in LDS (natural layout) and feed dP.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   constexpr int QB = RA_DKDV_BN, NMB = QB / 32;
-  constexpr int DT = D / 16, CB = D / 32, TILE = QB * (D + 8);
+  constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, QB>::ALLOC;
   __shared__ __attribute__((aligned(16))) half_t Qs[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Ds[2 * TILE];
-  __shared__ __attribute__((aligned(16))) half_t Vst[RA_DKDV_VLDS ? BM * (D + 8) : 8];
-  __shared__ __attribute__((aligned(16))) float lses[2 * QB];
-  __shared__ __attribute__((aligned(16))) float drs[2 * QB];
+  __shared__ __attribute__((aligned(16))) half_t Vst[BM * (D + 8)];
+  __shared__ __attribute__((aligned(16))) float rsl[2 * 2 * QB];
   __shared__ float red[4 * (D / 2)];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
@@ -411,24 +410,18 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   const size_t head = (size_t)bh * p.N * D;
   const half_t* qh = p.qh + head;
   const half_t* doh = p.doh + head;
-  const float* lse_h = p.lse + (size_t)bh * p.N;
-  const float* dr_h = p.drow + (size_t)bh * p.N;
+  const float* rs_h = p.rs + (size_t)bh * rs_groups(p.N) * 64;
 
-  half8 kf[DT], vf[RA_DKDV_VLDS ? 1 : DT];
+  half8 kf[DT];
   load_frag_rows<D>(kf, p.kh + head, key, p.N, g);
-  const half_t* vrow = nullptr;
-  if (RA_DKDV_VLDS) {
-    // rows k0 .. k0 + 127 of V, padded rows; lane reads row 32 w + l32
-    for (int ch = threadIdx.x; ch < BM * (D / 8); ch += 256) {
-      const int r = ch / (D / 8), c8 = ch % (D / 8);
-      const int row = min(k0 + r, p.N - 1);
-      *reinterpret_cast<half8*>(Vst + r * (D + 8) + c8 * 8) =
-          *reinterpret_cast<const half8*>(p.vh + head + (size_t)row * D + c8 * 8);
-    }
-    vrow = Vst + (32 * w + l32) * (D + 8) + 8 * g;
-  } else {
-    load_frag_rows<D>(vf, p.vh + head, key, p.N, g);
+  // rows k0 .. k0 + 127 of V, padded rows; lane reads row 32 w + l32
+  for (int ch = threadIdx.x; ch < BM * (D / 8); ch += 256) {
+    const int r = ch / (D / 8), c8 = ch % (D / 8);
+    const int row = min(k0 + r, p.N - 1);
+    *reinterpret_cast<half8*>(Vst + r * (D + 8) + c8 * 8) =
+        *reinterpret_cast<const half8*>(p.vh + head + (size_t)row * D + c8 * 8);
   }
+  const half_t* vrow = Vst + (32 * w + l32) * (D + 8) + 8 * g;
   f32x16 dk[CB], dv[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) { dk[cb] = f32x16{}; dv[cb] = f32x16{}; }
@@ -438,27 +431,17 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
 
   TileDMA<D, QB> dma;
   dma.init(lane, w);
-  float lv = INFINITY, dvv = 0.f;   // row scalars held by threads < QB
+  // one step's tiles; wave j < NMB also copies the row scalars of 32-row
+  // group j (lane i -> float i; qs0 is a multiple of 32)
   auto load_rows = [&](int r0, int buf) {
-    dma.load(Qs + buf * TILE, qh, r0, p.N, w);
-    dma.load(Ds + buf * TILE, doh, r0, p.N, w);
-    if (threadIdx.x < QB) {
-      const int row = r0 + threadIdx.x;
-      const bool ok = row < p.N;
-      lv = ok ? lse_h[ok ? row : 0] * LOG2E : INFINITY;
-      dvv = ok ? dr_h[ok ? row : 0] : 0.f;
-    }
+    dma.load(Qs + buf * TILE, qh, r0, p.N);
+    dma.load(Ds + buf * TILE, doh, r0, p.N);
+    if (dma.wave < NMB)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(rs_h + ((r0 >> 5) + dma.wave) * 64 + lane),
+          (__attribute__((address_space(3))) void*)(rsl + buf * 2 * QB + dma.wave * 64), 4, 0, 0);
   };
-  auto store_rows = [&](int buf) {
-    if (threadIdx.x < QB) {
-      lses[buf * QB + threadIdx.x] = lv;
-      drs[buf * QB + threadIdx.x] = dvv;
-    }
-  };
-  if (n_it > 0) {
-    load_rows(qs0, 0);
-    store_rows(0);
-  }
+  if (n_it > 0) load_rows(qs0, 0);
   wait_lds_copies();
   __syncthreads();
   // the first steps cross the workgroup's diagonal (masked), the rest need
@@ -467,13 +450,11 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   auto step = [&](int it, auto masked) {
     const int r0 = qs0 + it * QB;
     const int cur = it & 1;
-    const bool more = it + 1 < n_it;
-    if (more) load_rows(r0 + QB, cur ^ 1);
+    if (it + 1 < n_it) load_rows(r0 + QB, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (!(CAUSAL && wkey0 > r0 + QB - 1))  // skip tiles wholly before this wave's keys
       dkdv_tile<D, NMB, decltype(masked)::value>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
-                                                 lses + cur * QB, drs + cur * QB, kf, vf, vrow, r0,
-                                                 key, lane);
-    if (more) store_rows(cur ^ 1);
+                                                 rsl + cur * 2 * QB, kf, vrow, r0, key, lane);
     wait_lds_copies();
     __syncthreads();
   };

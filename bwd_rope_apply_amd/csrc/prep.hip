@@ -102,7 +102,21 @@ __global__ void prep_kernel(PrepParams p) {
     if (p.drow) {
       // the cpr lanes of a row are consecutive and aligned inside the wave
       for (int off = 1; off < cpr; off <<= 1) acc += __shfl_xor(acc, off, 64);
-      if (live && chunk == 0) p.drow[row] = acc;
+      if (live && chunk == 0) {
+        p.drow[row] = acc;
+        if (p.rs) {
+          const int G = rs_groups(p.N);
+          float* rsh = p.rs + (size_t)(row / p.N) * G * 64;
+          rsh[(pos >> 5) * 64 + (pos & 31)] = p.lse[row] * LOG2E;
+          rsh[(pos >> 5) * 64 + 32 + (pos & 31)] = acc;
+          if (pos == p.N - 1) {  // pad rows up to the end of the spare group
+            for (int r = p.N; r < 32 * G; ++r) {
+              rsh[(r >> 5) * 64 + (r & 31)] = INFINITY;
+              rsh[(r >> 5) * 64 + 32 + (r & 31)] = 0.f;
+            }
+          }
+        }
+      }
     }
   }
 }

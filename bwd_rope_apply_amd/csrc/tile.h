@@ -92,37 +92,60 @@ __device__ __forceinline__ int sig_inv(int P) {
 
 // Direct global -> LDS copy of one streamed [ROWS][D] fp16 tile into the
 // sig() layout, without passing through registers (global_load_lds_dwordx4:
-// each wave instruction writes 1 KiB of LDS, lane i at byte 16 i).  The tile
-// is covered by consecutive 1 KiB blocks, block b issued by wave b % 4; a
-// lane whose 16-byte slot falls in a row pad loads a dummy chunk.  Rows at or
-// past N are clamped to N - 1 (masked downstream).  Callers wait for the
-// copies (wait_lds_copies) before the barrier that publishes the tile.
+// each wave instruction writes 1 KiB of LDS, lane i at byte 16 i).  A tile
+// buffer is a whole number of 1 KiB blocks (ALLOC halfs), block b issued by
+// wave b % 4; a lane whose 16-byte slot falls in a row pad or past the tile
+// loads a dummy chunk (row 0), so every lane of an issued block loads and no
+// per-lane branch is needed.  Each lane's byte offset from the tile's first
+// row is computed once; a step adds the tile's row base in scalar registers.
+// Rows at or past N are clamped to N - 1 (masked downstream) on the one
+// path that needs it.  Callers wait for the copies (wait_lds_copies) before
+// the barrier that publishes the tile.
 template <int D, int ROWS>
 struct TileDMA {
   static constexpr int RB = (D + 8) * 2;                 // bytes per physical row
   static constexpr int BYTES = ROWS * RB;
   static constexpr int NBLK = (BYTES + 1023) / 1024;
   static constexpr int PER_WAVE = (NBLK + 3) / 4;
-  int lc[PER_WAVE];   // logical row * 64 + chunk; -1 row pad; -2 past the tile
-  __device__ __forceinline__ void init(int lane, int wave) {
+  static constexpr int ALLOC = NBLK * 512;               // halfs per tile buffer
+  uint32_t off[PER_WAVE];   // byte offset of this lane's chunk from row r0 (row * 2D + col)
+  int wave;                 // wave index (uniform)
+  __device__ __forceinline__ void init(int lane, int w) {
+    wave = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int o = (wave + 4 * i) * 1024 + 16 * lane;
+      const int o = (w + 4 * i) * 1024 + 16 * lane;
       const int pr = o / RB, within = o % RB;
-      lc[i] = (o >= BYTES) ? -2 : (within >= 2 * D ? -1 : sig_inv(pr) * 64 + within / 16);
+      const bool real = o < BYTES && within < 2 * D;
+      off[i] = real ? (uint32_t)(sig_inv(pr) * D * 2 + within) : 0u;
     }
   }
-  __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0, int N,
-                                       int wave) const {
+  // block wave + 4 i exists for every wave in the full rounds i < NBLK / 4
+  __device__ __forceinline__ bool issued(int i) const { return i < NBLK / 4 || wave + 4 * i < NBLK; }
+  // src is the head's plane; byte offsets within a plane fit 32 bits
+  // (N D 2 <= 2^32 for every accepted shape), so the address is a scalar
+  // base plus one zero-extended 32-bit lane offset: the scalar-base form
+  __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0, int N) const {
+    const char* base = reinterpret_cast<const char*>(src);
+    const uint32_t rb = (uint32_t)r0 * (uint32_t)(2 * D);
+    if (r0 + ROWS <= N) {
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int b = wave + 4 * i;
-      if (b < NBLK && lc[i] != -2) {
-        const int v = lc[i] < 0 ? 0 : lc[i];
-        const int row = min(r0 + (v >> 6), N - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(src + (size_t)row * D + (v & 63) * 8),
-            (__attribute__((address_space(3))) void*)(tile + b * 512), 16, 0, 0);
+      for (int i = 0; i < PER_WAVE; ++i) {
+        if (issued(i))
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(base + (rb + off[i])),
+              (__attribute__((address_space(3))) void*)(tile + (wave + 4 * i) * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        if (issued(i)) {
+          const int row = r0 + (int)(off[i] / (2 * D));
+          const uint32_t o = (uint32_t)min(row, N - 1) * (uint32_t)(2 * D) + off[i] % (2 * D);
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(base + o),
+              (__attribute__((address_space(3))) void*)(tile + (wave + 4 * i) * 512), 16, 0, 0);
+        }
       }
     }
   }
