@@ -437,9 +437,7 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     dma.load(Qs + buf * TILE, qh, r0, p.N);
     dma.load(Ds + buf * TILE, doh, r0, p.N);
     if (dma.wave < NMB)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(rs_h + ((r0 >> 5) + dma.wave) * 64 + lane),
-          (__attribute__((address_space(3))) void*)(rsl + buf * 2 * QB + dma.wave * 64), 4, 0, 0);
+      lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane, rsl + buf * 2 * QB + dma.wave * 64);
   };
   if (n_it > 0) load_rows(qs0, 0);
   wait_lds_copies();

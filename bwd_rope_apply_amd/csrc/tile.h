@@ -101,6 +101,37 @@ __device__ __forceinline__ int sig_inv(int P) {
 // Rows at or past N are clamped to N - 1 (masked downstream) on the one
 // path that needs it.  Callers wait for the copies (wait_lds_copies) before
 // the barrier that publishes the tile.
+// One lane-wise 16-byte (or 4-byte) global -> LDS copy: lane i writes LDS
+// bytes [lds + size i, lds + size (i + 1)) from gbase + voff (gbase and lds
+// uniform).  It is the same global_load_lds instruction the compiler's
+// builtin emits, written out so that the compiler does not treat it as a
+// pending LDS write: otherwise it waits for every copy in flight (the next
+// tile's included) before each LDS read of the current tile, which leaves
+// the double buffer nothing to overlap.  Callers wait for the copies
+// explicitly (wait_lds_copies) before the barrier that publishes a tile.
+// M0 carries the LDS address; the s_nop covers the wait states between the
+// scalar writes of M0 / the base and the copy's reads of them.
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(m0v)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(m0v)
+      : "memory", "m0");
+}
+
 template <int D, int ROWS>
 struct TileDMA {
   static constexpr int RB = (D + 8) * 2;                 // bytes per physical row
@@ -131,10 +162,7 @@ struct TileDMA {
     if (r0 + ROWS <= N) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        if (issued(i))
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(base + (rb + off[i])),
-              (__attribute__((address_space(3))) void*)(tile + (wave + 4 * i) * 512), 16, 0, 0);
+        if (issued(i)) lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
       }
     } else {
 #pragma unroll
@@ -142,9 +170,7 @@ struct TileDMA {
         if (issued(i)) {
           const int row = r0 + (int)(off[i] / (2 * D));
           const uint32_t o = (uint32_t)min(row, N - 1) * (uint32_t)(2 * D) + off[i] % (2 * D);
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(base + o),
-              (__attribute__((address_space(3))) void*)(tile + (wave + 4 * i) * 512), 16, 0, 0);
+          lds_copy16(base, o, tile + (wave + 4 * i) * 512);
         }
       }
     }
