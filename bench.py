@@ -9,9 +9,13 @@ U[-1, 0.5]) with inputs resident in device memory.  Prints one JSON line.
 Throughput is algorithmic: 6 B H N^2 D flops per step (the two forward
 products and the four backward products over the causal half), the standard
 count for causal attention training; recomputation of scores in the backward
-is not counted.  Per-stage durations come from HIP events recorded on the
-stream the library launches on (torch's current stream), between the staged
-entry points, so the timed work is exactly the full forward + backward.
+is not counted (the FlashAttention convention, which adds it, 7 B H N^2 D, is
+reported beside it).  Per-stage durations come from HIP events recorded on
+the stream the library launches on (torch's current stream), between the
+staged entry points, so the timed work is exactly the full forward +
+backward.  One workspace serves both passes: the backward reuses the
+forward's rotated fp16 planes and frequency table (saved activations) and
+prepares only dO and D.
 """
 from __future__ import annotations
 
@@ -27,7 +31,9 @@ HBM_GBS = 8000.0
 METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
 
 FWD_STAGES = [("fwd_prep", 1), ("fwd_exact", 2), ("fwd_main", 4)]
-BWD_STAGES = [("bwd_prep", 1), ("bwd_exact", 2), ("bwd_dq", 8), ("bwd_dkdv", 16),
+# the backward reuses the forward's table and operand planes from the shared
+# workspace (PREP_GRAD: it converts only dO and computes D)
+BWD_STAGES = [("bwd_prep", 64), ("bwd_exact", 2), ("bwd_dq", 8), ("bwd_dkdv", 16),
               ("bwd_dalpha", 32)]
 # algorithmic products carried by each matrix-core stage (units of B H N^2 D
 # flops, causal): fwd QK^T and PV; dQ; dV, dP and dK
@@ -126,8 +132,9 @@ def main():
     dq, dk, dv = (torch.empty((B, H, N, D), **f32) for _ in range(3))
     da = torch.empty((D // 2,), **f32)
     dt_code = _lib.BF16 if wl.dtype == "bf16" else _lib.FP32
-    ws_f = torch.empty(_lib.workspace_bytes("fwd", B, H, N, D, dt_code, wl.causal), dtype=torch.uint8, device=dev)
+    # one buffer for both passes (the forward's regions are a prefix of the backward's)
     ws_b = torch.empty(_lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal), dtype=torch.uint8, device=dev)
+    ws_f = ws_b
 
     names = [n for n, _ in FWD_STAGES] + [n for n, _ in BWD_STAGES]
     if args.copy_calibration:
@@ -172,6 +179,10 @@ def main():
 
     stage_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
                 for i, n in enumerate(names)}
+    nf = len(FWD_STAGES)
+    step_ev = np.array([ev[s][0].elapsed_time(ev[s][len(names)]) for s in range(args.steps)])
+    fwd_ev = np.array([ev[s][0].elapsed_time(ev[s][nf]) for s in range(args.steps)])
+    bwd_ev = np.array([ev[s][nf].elapsed_time(ev[s][len(names)]) for s in range(args.steps)])
     ms_step = wall * 1e3 / args.steps
     unit = float(B) * H * N * N * D
     flops = 6.0 * unit
@@ -202,6 +213,13 @@ def main():
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic, "avg_ms": round(stage_ms[dom], 4)},
         "stages_ms": {n: round(t, 4) for n, t in stage_ms.items()},
+        "events_ms": {"step_median": round(float(np.median(step_ev)), 4),
+                      "step_min": round(float(step_ev.min()), 4),
+                      "fwd_median": round(float(np.median(fwd_ev)), 4),
+                      "bwd_median": round(float(np.median(bwd_ev)), 4)},
+        "tflops_fwd": round(2.0 * unit / (float(np.median(fwd_ev)) * 1e-3) / 1e12, 2),
+        "tflops_bwd": round(4.0 * unit / (float(np.median(bwd_ev)) * 1e-3) / 1e12, 2),
+        "tflops_fa_convention": round(7.0 * unit / (ms_step * 1e-3) / 1e12, 2),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, wl)

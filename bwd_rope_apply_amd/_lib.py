@@ -19,6 +19,7 @@ FP32, BF16 = 0, 1
 # rope_attn_stage bits
 STAGE_PREP, STAGE_EXACT, STAGE_MAIN, STAGE_DQ, STAGE_DKDV, STAGE_DALPHA = 1, 2, 4, 8, 16, 32
 STAGE_ALL = 63
+STAGE_PREP_GRAD = 64   # backward: dO plane and D only, reusing the forward's workspace
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_HIP", -7: "ERR_ARG"}
 

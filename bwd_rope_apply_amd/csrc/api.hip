@@ -37,11 +37,14 @@ int check_shape(const Shape& s) {
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 // Workspace regions, in order.  Sizes are 0 for regions a call does not use.
+// The forward's regions (table, operand planes, corner low parts) come first
+// and are laid out identically by both passes, so a backward run on the
+// forward's workspace can reuse them (ROPE_ATTN_STAGE_PREP_GRAD).
 struct Layout {
-  size_t theta, cs, qh, kh, vh, doh, qlo, klo, drow, rs, dkp, dvp, part;
+  size_t theta, cs, qh, kh, vh, qlo, klo, doh, drow, rs, dkp, dvp, part;
   int slots;
   size_t total() const {
-    return theta + cs + qh + kh + vh + doh + qlo + klo + drow + rs + dkp + dvp + part;
+    return theta + cs + qh + kh + vh + qlo + klo + doh + drow + rs + dkp + dvp + part;
   }
 };
 
@@ -149,7 +152,6 @@ int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const vo
   half_t* qh = c.take<half_t>(L.qh);
   half_t* kh = c.take<half_t>(L.kh);
   half_t* vh = c.take<half_t>(L.vh);
-  c.take<half_t>(L.doh);
   half_t* qlo = c.take<half_t>(L.qlo);
   half_t* klo = c.take<half_t>(L.klo);
 
@@ -211,9 +213,9 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
   half_t* qh = c.take<half_t>(L.qh);
   half_t* kh = c.take<half_t>(L.kh);
   half_t* vh = c.take<half_t>(L.vh);
-  half_t* doh = c.take<half_t>(L.doh);
   half_t* qlo = c.take<half_t>(L.qlo);
   half_t* klo = c.take<half_t>(L.klo);
+  half_t* doh = c.take<half_t>(L.doh);
   float* drow = c.take<float>(L.drow);
   float* rs = c.take<float>(L.rs);
   float* dkp = c.take<float>(L.dkp);
@@ -228,13 +230,16 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
   const int n_dq = s.bf16() ? dq_mfma_slots(mp) : 0;
   const int n_dk = s.bf16() ? dkdv_mfma_slots(mp) : 0;
 
-  if (stages & ROPE_ATTN_STAGE_PREP) {
-    tables(s, base, alpha, theta, cs, hs);
+  if (stages & (ROPE_ATTN_STAGE_PREP | ROPE_ATTN_STAGE_PREP_GRAD)) {
+    // PREP_GRAD alone: the table and the Q~, K~, V planes are the forward's
+    const bool full = (stages & ROPE_ATTN_STAGE_PREP) != 0;
+    if (full) tables(s, base, alpha, theta, cs, hs);
     PrepParams pp = {};
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
-    pp.qh = qh; pp.kh = kh; pp.vh = vh; pp.doh = doh; pp.drow = drow;
+    pp.qh = full ? qh : nullptr; pp.kh = full ? kh : nullptr; pp.vh = full ? vh : nullptr;
+    pp.doh = doh; pp.drow = drow;
     pp.lse = lse; pp.rs = rs;
-    pp.qlo = qlo; pp.klo = klo; pp.rlo = s.corner();
+    pp.qlo = full ? qlo : nullptr; pp.klo = full ? klo : nullptr; pp.rlo = s.corner();
     pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
     pp.qscale = LOG2E / sqrtf((float)D);
     launch_prep(pp, hs);

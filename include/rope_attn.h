@@ -108,7 +108,17 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
  *   MAIN    forward matrix-core pass (bf16 inputs)
  *   DQ      dQ matrix-core pass (bf16 inputs)
  *   DKDV    dK, dV matrix-core pass (bf16 inputs)
- *   DALPHA  fixed-order reduction of the d alpha partials */
+ *   DALPHA  fixed-order reduction of the d alpha partials
+ *   PREP_GRAD  (backward only, in place of PREP) the dO plane and D_i only:
+ *           the frequency table and the Q~, K~, V planes are taken from the
+ *           workspace as the forward's PREP stage left them.  The caller
+ *           guarantees that this workspace buffer was last passed to
+ *           rope_attn_fwd / rope_attn_fwd_stages with PREP for the same q, k,
+ *           v, B, H, N, D, dtype, base, alpha and causal, and was not
+ *           modified since (the forward's regions are a prefix of the
+ *           backward's layout, so one buffer of rope_attn_bwd_workspace_bytes
+ *           serves both calls).  Violating this gives wrong results; it is
+ *           not detected. */
 typedef enum {
   ROPE_ATTN_STAGE_PREP = 1,
   ROPE_ATTN_STAGE_EXACT = 2,
@@ -116,7 +126,8 @@ typedef enum {
   ROPE_ATTN_STAGE_DQ = 8,
   ROPE_ATTN_STAGE_DKDV = 16,
   ROPE_ATTN_STAGE_DALPHA = 32,
-  ROPE_ATTN_STAGE_ALL = 63
+  ROPE_ATTN_STAGE_ALL = 63,
+  ROPE_ATTN_STAGE_PREP_GRAD = 64
 } rope_attn_stage;
 
 int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const void* v, float* o,

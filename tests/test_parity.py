@@ -107,6 +107,30 @@ def test_deterministic_and_overwrites_nan():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("name,N", [("long_8k", 333), ("tiny_fp32", 96)])
+def test_backward_reusing_forward_workspace(name, N):
+    """The backward's PREP_GRAD stage on the forward's workspace (rotated
+    planes and table reused, only dO and D prepared) gives bit-identical
+    results to a standalone backward with its own PREP."""
+    import torch
+    from bwd_rope_apply_amd import _lib, fwd, bwd
+    wl = W.get(name, B=1, H=2, N=N)
+    inp = W.make_inputs(wl)
+    q, k, v, do = (Hn.to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    a = Hn.to_device(inp.alpha)
+    dt = _lib.BF16 if wl.dtype == "bf16" else _lib.FP32
+    ws = torch.empty(_lib.workspace_bytes("bwd", 1, 2, N, wl.D, dt, wl.causal), dtype=torch.uint8,
+                     device="cuda")
+    o, lse = fwd(q, k, v, wl.base, a, wl.causal, workspace=ws)
+    ref = bwd(q, k, v, o, do, lse, wl.base, a, wl.causal)          # own workspace, full PREP
+    fwd(q, k, v, wl.base, a, wl.causal, workspace=ws, out=(o, lse))
+    st = _lib.STAGE_ALL & ~_lib.STAGE_PREP | _lib.STAGE_PREP_GRAD
+    got = bwd(q, k, v, o, do, lse, wl.base, a, wl.causal, workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, got):
+        assert torch.equal(x, y)
+
+
 def test_rotational_balance_on_gpu_gradients():
     """Per (b, h, m): sum_i wedge(q_i, dQ_i) + sum_j wedge(k_j, dK_j) = 0 holds
     for the GPU's own dQ, dK (a property, no oracle)."""
