@@ -46,6 +46,17 @@ scale 1/sqrt(D); positions 0..N-1 for both queries and keys; causal keeps
 j <= i; the scalar loss whose vector-Jacobian product is returned is
 L = sum(O * dO).
 
+Frequency-schedule variants (optional arguments, defaults = the above):
+  rot     partial RoPE: only pairs m < rot are rotated and the slower bands
+          m >= rot pass through (theta_hat_m = 0 there, so their alpha has
+          no effect and a zero gradient); LeRoPE's p-RoPE baseline, which
+          leaves the slowest 25% of bands unrotated ("Experimental setup",
+          baselines), is rot = 0.75 * D/2.
+  scale   the softmax scale on q.k (default 1/sqrt(D)); context-extension
+          schemes that LeRoPE combines with (named under "Extrapolation")
+          act through per-band alpha offsets and such a scale.
+  p0      the position of the first row, shared by queries and keys.
+
 Inputs are numpy arrays [B, H, N, D] of any float type (upcast exactly to
 float64); alpha is [D/2].
 """
@@ -62,10 +73,14 @@ def thetas(base: float, D: int) -> np.ndarray:
     return np.float64(base) ** (-2.0 * m / D)
 
 
-def theta_hat(base: float, alpha, D: int) -> np.ndarray:
-    """Effective frequency exp(alpha_m) * theta_m (LeRoPE, Central mechanism)."""
+def theta_hat(base: float, alpha, D: int, rot=None) -> np.ndarray:
+    """Effective frequency exp(alpha_m) * theta_m (LeRoPE, Central mechanism);
+    zero for the unrotated bands m >= rot (partial RoPE)."""
     a = np.zeros(D // 2) if alpha is None else np.asarray(alpha, dtype=np.float64)
-    return np.exp(a) * thetas(base, D)
+    th = np.exp(a) * thetas(base, D)
+    if rot is not None:
+        th = np.where(np.arange(D // 2) < rot, th, 0.0)
+    return th
 
 
 def angles(N: int, th: np.ndarray, p0: float = 0.0) -> np.ndarray:
@@ -124,9 +139,13 @@ def _softmax_grad(P, dP, Drow):
     return P * (dP - Drow[:, None])
 
 
-def _head_fwd(q, k, v, th, causal, p0, block):
+def _scale(D, scale):
+    return 1.0 / np.sqrt(D) if scale is None else float(scale)
+
+
+def _head_fwd(q, k, v, th, causal, p0, block, scale=None):
     N, D = q.shape
-    scale = 1.0 / np.sqrt(D)
+    scale = _scale(D, scale)
     phi = angles(N, th, p0)
     qt, kt = rotate(q, phi), rotate(k, phi)
     o = np.empty((N, D))
@@ -142,9 +161,9 @@ def _head_fwd(q, k, v, th, causal, p0, block):
     return o, lse
 
 
-def _head_bwd(q, k, v, o, do, lse, th, causal, p0, block):
+def _head_bwd(q, k, v, o, do, lse, th, causal, p0, block, scale=None):
     N, D = q.shape
-    scale = 1.0 / np.sqrt(D)
+    scale = _scale(D, scale)
     phi = angles(N, th, p0)
     qt, kt = rotate(q, phi), rotate(k, phi)
     Drow = (do * o).sum(axis=1)
@@ -179,46 +198,48 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def ref_fwd(q, k, v, base, alpha=None, causal=True, p0=0.0, block=512):
+def ref_fwd(q, k, v, base, alpha=None, causal=True, p0=0.0, block=512, scale=None, rot=None):
     """Returns (O [B,H,N,D], LSE [B,H,N]), float64; LSE is the natural-log
     log-sum-exp of the scaled, masked scores of each row."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, D = q.shape
-    th = theta_hat(base, alpha, D)
+    th = theta_hat(base, alpha, D, rot)
     o = np.empty((B, H, N, D))
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):  # heads are independent work units
-            o[b, h], lse[b, h] = _head_fwd(q[b, h], k[b, h], v[b, h], th, causal, p0, block)
+            o[b, h], lse[b, h] = _head_fwd(q[b, h], k[b, h], v[b, h], th, causal, p0, block, scale)
     return o, lse
 
 
-def ref_bwd(q, k, v, o, do, lse, base, alpha=None, causal=True, p0=0.0, block=512):
+def ref_bwd(q, k, v, o, do, lse, base, alpha=None, causal=True, p0=0.0, block=512, scale=None,
+            rot=None):
     """Returns (dQ, dK, dV [B,H,N,D] in the un-rotated frame, dalpha [D/2]):
     the vector-Jacobian product of (Q, K, V, alpha) -> O for the upstream
     gradient dO, given the forward's O and LSE."""
     q, k, v, o, do, lse = map(_f64, (q, k, v, o, do, lse))
     B, H, N, D = q.shape
-    th = theta_hat(base, alpha, D)
+    th = theta_hat(base, alpha, D, rot)
     dq = np.empty((B, H, N, D))
     dk = np.empty((B, H, N, D))
     dv = np.empty((B, H, N, D))
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = _head_bwd(
-                q[b, h], k[b, h], v[b, h], o[b, h], do[b, h], lse[b, h], th, causal, p0, block)
+                q[b, h], k[b, h], v[b, h], o[b, h], do[b, h], lse[b, h], th, causal, p0, block,
+                scale)
     return dq, dk, dv, dalpha_chain(q, k, dq, dk, th, p0)
 
 
-def ref_dense(q, k, v, do, base, alpha=None, causal=True, p0=0.0):
+def ref_dense(q, k, v, do, base, alpha=None, causal=True, p0=0.0, scale=None, rot=None):
     """Every intermediate of one call as full matrices, for tiny inputs:
     dict with S, P, O, LSE, D, dP, dS, dQ, dK, dV, dalpha, qt, kt, theta_hat."""
     q, k, v, do = map(_f64, (q, k, v, do))
     B, H, N, D = q.shape
-    th = theta_hat(base, alpha, D)
+    th = theta_hat(base, alpha, D, rot)
     phi = angles(N, th, p0)
     qt, kt = rotate(q, phi), rotate(k, phi)
-    scale = 1.0 / np.sqrt(D)
+    scale = _scale(D, scale)
     S = scale * np.einsum("bhid,bhjd->bhij", qt, kt)
     if causal:
         S = np.where(np.tril(np.ones((N, N), dtype=bool)), S, -np.inf)
@@ -238,7 +259,7 @@ def ref_dense(q, k, v, do, base, alpha=None, causal=True, p0=0.0):
 
 
 def ref_head_rows(q, k, v, do, base, alpha=None, causal=True, rows=(), cols=(),
-                  p0=0.0, block=512):
+                  p0=0.0, block=512, scale=None, rot=None):
     """One head ([N, D] arrays) at full length, outputs at sampled positions.
 
     Runs the forward of the whole head (O and LSE of every row are needed by
@@ -248,9 +269,9 @@ def ref_head_rows(q, k, v, do, base, alpha=None, causal=True, rows=(), cols=(),
     (un-rotated frame)."""
     q, k, v, do = map(_f64, (q, k, v, do))
     N, D = q.shape
-    th = theta_hat(base, alpha, D)
-    o, lse = _head_fwd(q, k, v, th, causal, p0, block)
-    scale = 1.0 / np.sqrt(D)
+    th = theta_hat(base, alpha, D, rot)
+    o, lse = _head_fwd(q, k, v, th, causal, p0, block, scale)
+    scale = _scale(D, scale)
     phi = angles(N, th, p0)
     qt, kt = rotate(q, phi), rotate(k, phi)
     Drow = (do * o).sum(axis=1)

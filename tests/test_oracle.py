@@ -28,8 +28,8 @@ def rel(a, b):
     return np.abs(a - b).max() / den
 
 
-def loss(q, k, v, do, base, alpha, causal, p0=0.0, block=512):
-    o, _ = ref.ref_fwd(q, k, v, base, alpha, causal, p0, block)
+def loss(q, k, v, do, base, alpha, causal, p0=0.0, block=512, scale=None, rot=None):
+    o, _ = ref.ref_fwd(q, k, v, base, alpha, causal, p0, block, scale=scale, rot=rot)
     return float((o * do).sum())
 
 
@@ -291,32 +291,93 @@ def test_autograd_through_complex_rotation(causal):
     assert rel(da, ta.grad.numpy()) < 1e-10
 
 
+@pytest.mark.parametrize("scale,rot,p0", [(0.3, 5, 7.0), (None, 0, 0.0), (0.11, 8, 1000.0)])
+def test_autograd_frequency_variants(scale, rot, p0):
+    """Partial RoPE, a softmax scale and a position offset, independently:
+    torch complex rotation of the first `rot` pairs only (the rest pass
+    through), torch SDPA with the given scale, torch autograd for Q, K, V and
+    alpha (whose slower, unrotated bands get zero gradient)."""
+    B, H, N, D = 1, 2, 40, 16
+    base, causal = 300.0, True
+    q, k, v, do = rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D)
+    a = rnd(D // 2, scale=0.4)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ta = torch.tensor(a, requires_grad=True)
+    m = torch.arange(D // 2, dtype=torch.float64)
+    live = (m < rot).double()
+    th = torch.exp(ta) * base ** (-2.0 * m / D)
+    pos = torch.arange(N, dtype=torch.float64) + p0
+    e = torch.polar(torch.ones(N, D // 2, dtype=torch.float64), pos[:, None] * (th * live)[None, :])
+
+    def rot_(x):
+        z = torch.view_as_complex(x.reshape(B, H, N, D // 2, 2).contiguous())
+        return torch.view_as_real(z * e).reshape(B, H, N, D)
+
+    to = torch.nn.functional.scaled_dot_product_attention(rot_(tq), rot_(tk), tv, is_causal=causal,
+                                                          scale=scale)
+    (to * torch.tensor(do)).sum().backward()
+    kw = dict(scale=scale, rot=rot)
+    o, l = ref.ref_fwd(q, k, v, base, a, causal, p0, block=9, **kw)
+    assert rel(o, to.detach().numpy()) < 1e-12
+    dq, dk, dv, da = ref.ref_bwd(q, k, v, o, do, l, base, a, causal, p0, block=9, **kw)
+    assert rel(dq, tq.grad.numpy()) < 1e-10
+    assert rel(dk, tk.grad.numpy()) < 1e-10
+    assert rel(dv, tv.grad.numpy()) < 1e-11
+    tg = ta.grad.numpy()
+    assert np.abs(tg[rot:]).max(initial=0.0) == 0.0 and np.abs(da[rot:]).max(initial=0.0) == 0.0
+    if rot > 0:
+        # the offset term of dalpha cancels by rotational balance, so with a
+        # large offset the two sides agree to the size of that cancellation
+        assert rel(da[:rot], tg[:rot]) < (1e-10 if p0 < 100 else 1e-8)
+
+
+def test_scale_is_query_scaling():
+    """A softmax scale c / sqrt(D) equals the default scale on queries
+    multiplied by c (the rotation is linear): same O and LSE, dQ multiplied
+    by c, the same dK, dV and dalpha."""
+    B, H, N, D, c = 2, 2, 33, 8, 1.7
+    q, k, v, do = rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D)
+    a = rnd(D // 2, scale=0.3)
+    o1, l1 = ref.ref_fwd(q, k, v, 50.0, a, True, block=8, scale=c / math.sqrt(D))
+    o2, l2 = ref.ref_fwd(c * q, k, v, 50.0, a, True, block=8)
+    assert rel(o1, o2) < 1e-13 and np.abs(l1 - l2).max() < 1e-12
+    g1 = ref.ref_bwd(q, k, v, o1, do, l1, 50.0, a, True, block=8, scale=c / math.sqrt(D))
+    g2 = ref.ref_bwd(c * q, k, v, o2, do, l2, 50.0, a, True, block=8)
+    assert rel(g1[0], c * g2[0]) < 1e-12
+    for x, y in zip(g1[1:], g2[1:]):
+        assert rel(x, y) < 1e-12
+
+
 # ---------------------------------------------------- finite differences
 FD_CASES = [
-    (1, 4, 10.0, True), (2, 8, 1e4, True), (5, 4, 10.0, True), (16, 8, 1e4, True),
-    (5, 8, 1e4, False), (16, 4, 10.0, False),
+    (1, 4, 10.0, True, None, None), (2, 8, 1e4, True, None, None), (5, 4, 10.0, True, None, None),
+    (16, 8, 1e4, True, None, None), (5, 8, 1e4, False, None, None), (16, 4, 10.0, False, None, None),
+    # frequency-schedule variants: softmax scale and partial rotation
+    (5, 8, 1e4, True, 0.21, 3), (9, 8, 10.0, False, 0.6, 1), (6, 4, 10.0, True, None, 0),
 ]
 
 
-@pytest.mark.parametrize("N,D,base,causal", FD_CASES)
-def test_finite_differences_all_gradients(N, D, base, causal):
+@pytest.mark.parametrize("N,D,base,causal,scale,rot", FD_CASES)
+def test_finite_differences_all_gradients(N, D, base, causal, scale, rot):
     """Central differences (h = 1e-6) of L = sum(O * dO) over every entry of
-    Q, K, V and every alpha_m, B = 1, H = 2."""
+    Q, K, V and every alpha_m, B = 1, H = 2 (also at a non-default softmax
+    scale and with only the first `rot` bands rotated)."""
     B, H, h = 1, 2, 1e-6
     rng = np.random.default_rng(N * 100 + D + int(causal))
     q, k, v, do = (rng.normal(size=(B, H, N, D)) for _ in range(4))
     a = rng.normal(0, 0.3, size=D // 2)
     blk = 3
-    o, l = ref.ref_fwd(q, k, v, base, a, causal, block=blk)
-    grads = ref.ref_bwd(q, k, v, o, do, l, base, a, causal, block=blk)
+    kw = dict(scale=scale, rot=rot)
+    o, l = ref.ref_fwd(q, k, v, base, a, causal, block=blk, **kw)
+    grads = ref.ref_bwd(q, k, v, o, do, l, base, a, causal, block=blk, **kw)
     for gi, x in enumerate((q, k, v)):
         fd = np.zeros_like(x)
         for idx in np.ndindex(x.shape):
             x0 = x[idx]
             x[idx] = x0 + h
-            lp = loss(q, k, v, do, base, a, causal, block=blk)
+            lp = loss(q, k, v, do, base, a, causal, block=blk, **kw)
             x[idx] = x0 - h
-            lm = loss(q, k, v, do, base, a, causal, block=blk)
+            lm = loss(q, k, v, do, base, a, causal, block=blk, **kw)
             x[idx] = x0
             fd[idx] = (lp - lm) / (2 * h)
         assert np.abs(fd - grads[gi]).max() < 1e-7 * max(1.0, np.abs(fd).max()), gi
@@ -324,9 +385,9 @@ def test_finite_differences_all_gradients(N, D, base, causal):
     for m in range(a.size):
         a0 = a[m]
         a[m] = a0 + h
-        lp = loss(q, k, v, do, base, a, causal, block=blk)
+        lp = loss(q, k, v, do, base, a, causal, block=blk, **kw)
         a[m] = a0 - h
-        lm = loss(q, k, v, do, base, a, causal, block=blk)
+        lm = loss(q, k, v, do, base, a, causal, block=blk, **kw)
         a[m] = a0
         fa[m] = (lp - lm) / (2 * h)
     assert np.abs(fa - grads[3]).max() < 1e-7 * max(1.0, np.abs(fa).max())

@@ -12,8 +12,8 @@ from oracle import ref
 import test_oracle as pins
 
 PIN_SET = [
-    ("fd_causal", lambda: pins.test_finite_differences_all_gradients(5, 4, 10.0, True)),
-    ("fd_full", lambda: pins.test_finite_differences_all_gradients(5, 8, 1e4, False)),
+    ("fd_causal", lambda: pins.test_finite_differences_all_gradients(5, 4, 10.0, True, None, None)),
+    ("fd_full", lambda: pins.test_finite_differences_all_gradients(5, 8, 1e4, False, None, None)),
     ("textbook", pins.test_alpha_zero_is_textbook_complex_rope),
     ("alpha_base", pins.test_alpha_trades_against_base),
     ("offset", lambda: pins.test_relative_offset_invariance(True)),
@@ -25,6 +25,9 @@ PIN_SET = [
     ("sdpa", lambda: pins.test_zero_rotation_is_sdpa(True)),
     ("autograd", lambda: pins.test_autograd_through_complex_rotation(True)),
     ("dalpha3", lambda: pins.test_dalpha_three_derivations(True)),
+    ("variants_autograd", lambda: pins.test_autograd_frequency_variants(0.3, 5, 7.0)),
+    ("scale_is_query_scaling", pins.test_scale_is_query_scaling),
+    ("fd_variant", lambda: pins.test_finite_differences_all_gradients(5, 8, 1e4, True, 0.21, 3)),
 ]
 
 
@@ -80,15 +83,28 @@ def _mut_lse_drops_sum(S):
     return S.max(axis=1)
 
 
+def _mut_theta_hat_ignores_rot(base, alpha, D, rot=None):
+    return _orig_theta_hat(base, alpha, D)
+
+
+def _mut_theta_hat_rot_off_by_one(base, alpha, D, rot=None):
+    return _orig_theta_hat(base, alpha, D, None if rot is None else rot + 1)
+
+
+_orig_theta_hat = ref.theta_hat
 _orig_dalpha = ref.dalpha_chain
 _orig_head_bwd = ref._head_bwd
 
 
 def _mut_head_bwd(variant):
     """A copy of the per-head backward with one planted mistake."""
-    def f(q, k, v, o, do, lse, th, causal, p0, block):
+    def f(q, k, v, o, do, lse, th, causal, p0, block, scale=None):
         N, D = q.shape
-        scale = 1.0 / np.sqrt(D)
+        scale = ref._scale(D, scale)
+        if variant == "dk_default_scale":
+            dk_scale = 1.0 / np.sqrt(D)
+        else:
+            dk_scale = scale
         phi = ref.angles(N, th, p0)
         qt, kt = ref.rotate(q, phi), ref.rotate(k, phi)
         Drow = (do * o).sum(axis=1)
@@ -109,7 +125,7 @@ def _mut_head_bwd(variant):
             if variant == "dk_transposed" and dS.shape[0] == dS.shape[1]:
                 dkt[:ke] += scale * (dS @ qt[r0:r1])
             else:
-                dkt[:ke] += scale * (dS.T @ qt[r0:r1])
+                dkt[:ke] += dk_scale * (dS.T @ qt[r0:r1])
         if variant == "dk_rotated_frame":
             return ref.unrotate(dqt, phi), dkt, dv
         return ref.unrotate(dqt, phi), ref.unrotate(dkt, phi), dv
@@ -131,6 +147,9 @@ MUTANTS = {
     "dk_transposed": ("_head_bwd", _mut_head_bwd("dk_transposed")),
     "dq_no_scale": ("_head_bwd", _mut_head_bwd("dq_no_scale")),
     "dk_left_in_rotated_frame": ("_head_bwd", _mut_head_bwd("dk_rotated_frame")),
+    "dk_ignores_scale_argument": ("_head_bwd", _mut_head_bwd("dk_default_scale")),
+    "partial_rope_ignored": ("theta_hat", _mut_theta_hat_ignores_rot),
+    "partial_rope_one_band_too_many": ("theta_hat", _mut_theta_hat_rot_off_by_one),
 }
 
 
