@@ -47,6 +47,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unrotated-pairs", type=int, default=0,
+                    help="frequency-schedule option: leave the slowest bands unrotated (partial "
+                         "RoPE; D/8 is LeRoPE's p-RoPE baseline)")
+    ap.add_argument("--scale", type=float, default=0.0,
+                    help="frequency-schedule option: softmax scale (0 = 1/sqrt(D))")
+    ap.add_argument("--pos-offset", type=int, default=0,
+                    help="frequency-schedule option: position of row 0")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_8k.json"),
                     help="JSON with measured HBM bytes per launch of the MFMA kernels (used only "
                          "if it was taken on the current kernel source)")
@@ -137,6 +144,10 @@ def main():
     ws_f = ws_b
 
     names = [n for n, _ in FWD_STAGES] + [n for n, _ in BWD_STAGES]
+    opts = None
+    if args.unrotated_pairs or args.scale or args.pos_offset:
+        opts = dict(unrotated_pairs=args.unrotated_pairs, scale=args.scale,
+                    pos_offset=args.pos_offset)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -150,13 +161,14 @@ def main():
         for name, bit in FWD_STAGES:
             if events is not None:
                 events[i].record()
-            _lib.fwd(q, k, v, wl.base, alpha, wl.causal, workspace=ws_f, out=(o, lse), stages=bit)
+            _lib.fwd(q, k, v, wl.base, alpha, wl.causal, workspace=ws_f, out=(o, lse), stages=bit,
+                     opts=opts)
             i += 1
         for name, bit in BWD_STAGES:
             if events is not None:
                 events[i].record()
             _lib.bwd(q, k, v, o, do, lse, wl.base, alpha, wl.causal, workspace=ws_b,
-                     out=(dq, dk, dv, da), stages=bit)
+                     out=(dq, dk, dv, da), stages=bit, opts=opts)
             i += 1
         if events is not None:
             events[i].record()
@@ -208,6 +220,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
                    "base": wl.base, "storage": wl.dtype, "outputs": "fp32",
+                   "options": opts,
                    "flops_per_step": flops, "pct_bf16_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),

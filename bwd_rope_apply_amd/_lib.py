@@ -26,6 +26,21 @@ STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_AL
 _lib = None
 
 
+class Options(ctypes.Structure):
+    """rope_attn_options: unrotated_pairs (the slowest bands left unrotated,
+    partial RoPE), scale (softmax scale, 0 = 1/sqrt(D)), pos_offset (position
+    of row 0)."""
+    _fields_ = [("unrotated_pairs", ctypes.c_int), ("scale", ctypes.c_float),
+                ("pos_offset", ctypes.c_int)]
+
+
+def _opts(opts):
+    """None, an Options, or a dict with any of its fields."""
+    if opts is None or isinstance(opts, Options):
+        return opts
+    return Options(**opts)
+
+
 class RopeAttnError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} failed: status {status} ({STATUS.get(status, '?')}): {msg}")
@@ -54,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.rope_attn_fwd_stages.restype = i
     lib.rope_attn_bwd_stages.argtypes = [ctypes.c_uint] + lib.rope_attn_bwd.argtypes
     lib.rope_attn_bwd_stages.restype = i
+    lib.rope_attn_fwd_ex.argtypes = [ctypes.c_uint, vp] + lib.rope_attn_fwd.argtypes
+    lib.rope_attn_fwd_ex.restype = i
+    lib.rope_attn_bwd_ex.argtypes = [ctypes.c_uint, vp] + lib.rope_attn_bwd.argtypes
+    lib.rope_attn_bwd_ex.restype = i
     lib.rope_attn_status_string.argtypes = [i]
     lib.rope_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -113,9 +132,10 @@ def workspace_bytes(kind: str, B: int, H: int, N: int, D: int, dtype: int, causa
 
 
 def fwd(q, k, v, base: float, alpha=None, causal: bool = True, workspace=None,
-        out: Optional[Tuple] = None, stages: int = STAGE_ALL):
+        out: Optional[Tuple] = None, stages: int = STAGE_ALL, opts=None):
     """O [B,H,N,D] float32 and LSE [B,H,N] float32 for rotated attention.
-    ``stages`` selects rope_attn_fwd_stages bits (default: the whole pass)."""
+    ``stages`` selects stage bits (default: the whole pass); ``opts`` is None,
+    an Options or a dict of its fields (frequency-schedule options)."""
     import torch
     lib = load()
     B, H, N, D = _shape(q, k, v)
@@ -129,17 +149,19 @@ def fwd(q, k, v, base: float, alpha=None, causal: bool = True, workspace=None,
     nbytes = workspace_bytes("fwd", B, H, N, D, dt, causal)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.rope_attn_fwd_stages(stages, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
-                                  D, dt, float(base), _ptr(alpha), int(causal), _ptr(workspace),
-                                  workspace.numel(), _stream(q.device))
+    op = _opts(opts)
+    st = lib.rope_attn_fwd_ex(stages, None if op is None else ctypes.addressof(op), _ptr(q), _ptr(k),
+                              _ptr(v), _ptr(o), _ptr(lse), B, H, N, D, dt, float(base), _ptr(alpha),
+                              int(causal), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check("rope_attn_fwd", st)
     return o, lse
 
 
 def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, workspace=None,
-        want_dalpha: bool = True, out: Optional[Tuple] = None, stages: int = STAGE_ALL):
+        want_dalpha: bool = True, out: Optional[Tuple] = None, stages: int = STAGE_ALL, opts=None):
     """(dQ, dK, dV [B,H,N,D] float32, dalpha [D/2] float32 or None).
-    ``stages`` selects rope_attn_bwd_stages bits (default: the whole pass)."""
+    ``stages`` selects stage bits (default: the whole pass); ``opts`` as for
+    fwd (the same options as the forward that produced o, lse)."""
     import torch
     lib = load()
     B, H, N, D = _shape(q, k, v)
@@ -161,9 +183,10 @@ def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, works
     nbytes = workspace_bytes("bwd", B, H, N, D, dt, causal)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.rope_attn_bwd_stages(stages, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
-                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), B, H, N, D, dt,
-                                  float(base), _ptr(alpha), int(causal), _ptr(workspace),
-                                  workspace.numel(), _stream(q.device))
+    op = _opts(opts)
+    st = lib.rope_attn_bwd_ex(stages, None if op is None else ctypes.addressof(op), _ptr(q), _ptr(k),
+                              _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(da), B, H, N, D, dt, float(base), _ptr(alpha), int(causal),
+                              _ptr(workspace), workspace.numel(), _stream(q.device))
     _check("rope_attn_bwd", st)
     return dq, dk, dv, da

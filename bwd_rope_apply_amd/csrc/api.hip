@@ -36,6 +36,27 @@ int check_shape(const Shape& s) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// Frequency-schedule options with their defaults resolved.
+struct Opts {
+  int rot;      // rotated bands (D/2 - unrotated_pairs)
+  float scale;  // softmax scale
+  int pos0;     // position of row 0
+};
+
+int resolve(const rope_attn_options* o, const Shape& s, Opts& r) {
+  r.rot = s.D / 2;
+  r.scale = 1.0f / sqrtf((float)s.D);
+  r.pos0 = 0;
+  if (!o) return ROPE_ATTN_OK;
+  if (o->unrotated_pairs < 0 || o->unrotated_pairs > s.D / 2) return ROPE_ATTN_ERR_ARG;
+  if (!(o->scale == 0.0f || (isfinite(o->scale) && o->scale > 0.0f))) return ROPE_ATTN_ERR_ARG;
+  if (o->pos_offset < 0 || (long)o->pos_offset + s.N > (1L << 30)) return ROPE_ATTN_ERR_ARG;
+  r.rot = s.D / 2 - o->unrotated_pairs;
+  if (o->scale != 0.0f) r.scale = o->scale;
+  r.pos0 = o->pos_offset;
+  return ROPE_ATTN_OK;
+}
+
 // Workspace regions, in order.  Sizes are 0 for regions a call does not use.
 // The forward's regions (table, operand planes, corner low parts) come first
 // and are laid out identically by both passes, so a backward run on the
@@ -48,13 +69,13 @@ struct Layout {
   }
 };
 
-MfmaParams mfma_base(const Shape& s) {
+MfmaParams mfma_base(const Shape& s, float scale) {
   MfmaParams m = {};
   m.B = s.B; m.H = s.H; m.N = s.N; m.D = s.D;
   m.corner = s.corner();
   m.causal = s.causal;
   m.bf16 = s.bf16();
-  m.scale = 1.0f / sqrtf((float)s.D);
+  m.scale = scale;
   return m;
 }
 
@@ -73,7 +94,7 @@ Layout layout(const Shape& s, bool bwd) {
     if (s.bf16()) L.rs = up(sizeof(float) * s.bh() * rs_groups(s.N) * 64);
     if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * s.corner() * s.D);
     if (s.bf16()) {
-      const MfmaParams m = mfma_base(s);
+      const MfmaParams m = mfma_base(s, 1.0f);
       L.slots = (s.corner() ? corner_dq_slots(m) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
     } else {
       L.slots = 2 * simt_slots((int)s.bh(), s.N);
@@ -104,10 +125,11 @@ int check_common(const Shape& s, double base, void* ws, size_t ws_bytes, bool bw
   return ROPE_ATTN_OK;
 }
 
-void tables(const Shape& s, double base, const float* alpha, double* theta, float2* cs,
-            hipStream_t st) {
+void tables(const Shape& s, const Opts& op, double base, const float* alpha, double* theta,
+            float2* cs, hipStream_t st) {
   TableParams t = {};
   t.cs = cs; t.theta_hat = theta; t.alpha = alpha; t.base = base; t.N = s.N; t.D = s.D;
+  t.rot = op.rot; t.pos0 = op.pos0;
   launch_table(t, st);
 }
 
@@ -132,16 +154,19 @@ size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int 
   return layout(s, true).total();
 }
 
-int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const void* v, float* o,
-                         float* lse, int B, int H, int N, int D, int dtype, double base,
-                         const float* alpha, int causal, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void* q, const void* k,
+                     const void* v, float* o, float* lse, int B, int H, int N, int D, int dtype,
+                     double base, const float* alpha, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   const Shape s{B, H, N, D, dtype, causal};
   if (!q || !k || !v || !o || !lse) return ROPE_ATTN_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
       misaligned(alpha))
     return ROPE_ATTN_ERR_ALIGN;
   int st = check_common(s, base, workspace, workspace_bytes, false);
+  if (st) return st;
+  Opts op;
+  st = resolve(opts, s, op);
   if (st) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -156,24 +181,24 @@ int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const vo
   half_t* klo = c.take<half_t>(L.klo);
 
   if (stages & ROPE_ATTN_STAGE_PREP) {
-    tables(s, base, alpha, theta, cs, hs);
+    tables(s, op, base, alpha, theta, cs, hs);
     if (s.bf16()) {
       PrepParams pp = {};
       pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
       pp.qlo = qlo; pp.klo = klo; pp.rlo = s.corner();
       pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
-      pp.qscale = LOG2E / sqrtf((float)D);
+      pp.qscale = LOG2E * op.scale;
       launch_prep(pp, hs);
     }
   }
-  MfmaParams mp = mfma_base(s);
+  MfmaParams mp = mfma_base(s, op.scale);
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.qlo = qlo; mp.klo = klo; mp.o = o; mp.out_lse = lse;
   if (stages & ROPE_ATTN_STAGE_EXACT) {
     if (!s.bf16()) {
       SimtParams sp = {};
       sp.q = q; sp.k = k; sp.v = v; sp.cs = cs; sp.out_o = o; sp.out_lse = lse;
       sp.bf16 = 0; sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
-      sp.scale = 1.0f / sqrtf((float)D);
+      sp.scale = op.scale;
       sp.rows = N;
       launch_simt_fwd(sp, hs);
     } else if (s.corner()) {
@@ -187,15 +212,23 @@ int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const vo
 int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
                   int N, int D, int dtype, double base, const float* alpha, int causal,
                   void* workspace, size_t workspace_bytes, void* stream) {
-  return rope_attn_fwd_stages(ROPE_ATTN_STAGE_ALL, q, k, v, o, lse, B, H, N, D, dtype, base, alpha,
-                              causal, workspace, workspace_bytes, stream);
+  return rope_attn_fwd_ex(ROPE_ATTN_STAGE_ALL, nullptr, q, k, v, o, lse, B, H, N, D, dtype, base,
+                          alpha, causal, workspace, workspace_bytes, stream);
 }
 
-int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const void* v,
-                         const float* o, const void* dO, const float* lse, float* dq, float* dk,
-                         float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
-                         double base, const float* alpha, int causal, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+int rope_attn_fwd_stages(unsigned stages, const void* q, const void* k, const void* v, float* o,
+                         float* lse, int B, int H, int N, int D, int dtype, double base,
+                         const float* alpha, int causal, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return rope_attn_fwd_ex(stages, nullptr, q, k, v, o, lse, B, H, N, D, dtype, base, alpha, causal,
+                          workspace, workspace_bytes, stream);
+}
+
+int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void* q, const void* k,
+                     const void* v, const float* o, const void* dO, const float* lse, float* dq,
+                     float* dk, float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
+                     double base, const float* alpha, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   const Shape s{B, H, N, D, dtype, causal};
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ROPE_ATTN_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dO) ||
@@ -203,6 +236,9 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
       misaligned(dalpha))
     return ROPE_ATTN_ERR_ALIGN;
   int st = check_common(s, base, workspace, workspace_bytes, true);
+  if (st) return st;
+  Opts op;
+  st = resolve(opts, s, op);
   if (st) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -224,7 +260,7 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
 
   // d alpha partial slots: [exact or corner dQ rows | exact dK rows | MFMA dQ | MFMA dK]
   const int BHi = (int)s.bh();
-  MfmaParams mp = mfma_base(s);
+  MfmaParams mp = mfma_base(s, op.scale);
   const int n_exact_dq = s.bf16() ? (s.corner() ? corner_dq_slots(mp) : 0) : simt_slots(BHi, N);
   const int n_exact_dk = s.bf16() ? 0 : simt_slots(BHi, N);
   const int n_dq = s.bf16() ? dq_mfma_slots(mp) : 0;
@@ -233,7 +269,7 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
   if (stages & (ROPE_ATTN_STAGE_PREP | ROPE_ATTN_STAGE_PREP_GRAD)) {
     // PREP_GRAD alone: the table and the Q~, K~, V planes are the forward's
     const bool full = (stages & ROPE_ATTN_STAGE_PREP) != 0;
-    if (full) tables(s, base, alpha, theta, cs, hs);
+    if (full) tables(s, op, base, alpha, theta, cs, hs);
     PrepParams pp = {};
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
     pp.qh = full ? qh : nullptr; pp.kh = full ? kh : nullptr; pp.vh = full ? vh : nullptr;
@@ -241,7 +277,7 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
     pp.lse = lse; pp.rs = rs;
     pp.qlo = full ? qlo : nullptr; pp.klo = full ? klo : nullptr; pp.rlo = s.corner();
     pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
-    pp.qscale = LOG2E / sqrtf((float)D);
+    pp.qscale = LOG2E * op.scale;
     launch_prep(pp, hs);
   }
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.qlo = qlo; mp.klo = klo; mp.q = q; mp.k = k;
@@ -253,7 +289,7 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
       sp.q = q; sp.k = k; sp.v = v; sp.dO = dO; sp.o = o; sp.lse = lse; sp.drow = drow; sp.cs = cs;
       sp.dq = dq; sp.dk = dk; sp.dv = dv; sp.dalpha_part = part;
       sp.bf16 = 0; sp.BH = BHi; sp.N = N; sp.D = D; sp.causal = causal;
-      sp.scale = 1.0f / sqrtf((float)D);
+      sp.scale = op.scale;
       sp.rows = N; sp.qend = N; sp.final_ = 1;
       sp.slot0 = 0;
       launch_simt_dq(sp, hs);
@@ -286,8 +322,17 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
                   const float* lse, float* dq, float* dk, float* dv, float* dalpha, int B, int H,
                   int N, int D, int dtype, double base, const float* alpha, int causal,
                   void* workspace, size_t workspace_bytes, void* stream) {
-  return rope_attn_bwd_stages(ROPE_ATTN_STAGE_ALL, q, k, v, o, dO, lse, dq, dk, dv, dalpha, B, H,
-                              N, D, dtype, base, alpha, causal, workspace, workspace_bytes, stream);
+  return rope_attn_bwd_ex(ROPE_ATTN_STAGE_ALL, nullptr, q, k, v, o, dO, lse, dq, dk, dv, dalpha, B,
+                          H, N, D, dtype, base, alpha, causal, workspace, workspace_bytes, stream);
+}
+
+int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const void* v,
+                         const float* o, const void* dO, const float* lse, float* dq, float* dk,
+                         float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
+                         double base, const float* alpha, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return rope_attn_bwd_ex(stages, nullptr, q, k, v, o, dO, lse, dq, dk, dv, dalpha, B, H, N, D,
+                          dtype, base, alpha, causal, workspace, workspace_bytes, stream);
 }
 
 const char* rope_attn_status_string(int status) {
@@ -299,7 +344,9 @@ const char* rope_attn_status_string(int status) {
     case ROPE_ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case ROPE_ATTN_ERR_WORKSPACE: return "workspace smaller than the *_workspace_bytes query";
     case ROPE_ATTN_ERR_HIP: return "HIP runtime reported a launch error";
-    case ROPE_ATTN_ERR_ARG: return "base must be finite and > 0, causal must be 0 or 1";
+    case ROPE_ATTN_ERR_ARG:
+      return "base must be finite and > 0, causal 0 or 1; options: unrotated_pairs in [0, D/2], "
+             "scale 0 (default) or finite > 0, pos_offset >= 0 with pos_offset + N <= 2^30";
     default: return "unknown status";
   }
 }

@@ -38,11 +38,13 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // ------------------------------------------------------------------ params
 struct TableParams {
-  float2* cs;           // [N][D/2] (cos, sin) of p * theta_hat_m
-  double* theta_hat;    // [D/2]
+  float2* cs;           // [N][D/2] (cos, sin) of (p + pos0) * theta_hat_m
+  double* theta_hat;    // [D/2]; 0 for the unrotated bands m >= rot
   const float* alpha;   // [D/2] or null (all zero)
   double base;
   int N, D;
+  int rot;              // bands m < rot are rotated (partial RoPE), D/2 = all
+  int pos0;             // position of row 0
 };
 
 struct PrepParams {

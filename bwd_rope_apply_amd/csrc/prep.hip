@@ -16,10 +16,12 @@ __global__ void table_kernel(TableParams p) {
   const int m = (int)(idx % half);
   const int pos = (int)(idx / half);
   const double a = p.alpha ? (double)p.alpha[m] : 0.0;
-  const double th = exp(a) * pow(p.base, -2.0 * (double)m / (double)p.D);
+  // unrotated bands (partial RoPE) have rate 0: angle 0, and a zero alpha
+  // gradient through the theta_hat factor
+  const double th = m < p.rot ? exp(a) * pow(p.base, -2.0 * (double)m / (double)p.D) : 0.0;
   if (pos == 0) p.theta_hat[m] = th;
   double s, c;
-  sincos((double)pos * th, &s, &c);
+  sincos((double)(pos + p.pos0) * th, &s, &c);
   p.cs[idx] = make_float2((float)c, (float)s);
 }
 

@@ -141,6 +141,47 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
                          double base, const float* alpha, int causal, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Frequency-schedule options (a zero-initialised struct, or a NULL pointer,
+ * means the defaults, i.e. exactly rope_attn_fwd / rope_attn_bwd):
+ *   unrotated_pairs  the slowest `unrotated_pairs` bands m >= D/2 -
+ *           unrotated_pairs pass through unrotated (partial RoPE: their
+ *           effective rate is 0, so alpha has no effect there and dalpha is
+ *           0).  LeRoPE ("Experimental setup", baselines) compares against
+ *           p-RoPE, which removes the rotation from the slowest 25% of the
+ *           bands: unrotated_pairs = D/8.  Range [0, D/2].
+ *   scale   softmax scale on q.k; 0 = 1/sqrt(D).  Context-extension schemes
+ *           that LeRoPE is combined with (its "Extrapolation" result) act
+ *           through per-band offsets, which are alpha, and such a scale.
+ *           Finite and > 0 when nonzero.
+ *   pos_offset  position of row 0, shared by queries and keys (rows sit at
+ *           pos_offset .. pos_offset + N - 1).  Outputs depend on positions
+ *           only through their differences (LeRoPE, "Problem statement":
+ *           relative position through the rotation), so this tests large
+ *           absolute angles; dalpha uses positions relative to row 0, which
+ *           equals the absolute-position form because the per-band wedge
+ *           sums of the query and key gradients cancel.  >= 0 with
+ *           pos_offset + N <= 2^30.
+ * Invalid options return ROPE_ATTN_ERR_ARG before any launch. */
+typedef struct {
+  int unrotated_pairs;
+  float scale;
+  int pos_offset;
+} rope_attn_options;
+
+/* The staged forward and backward with options (opts may be NULL).  A
+ * backward run with PREP_GRAD must use the same options as the forward that
+ * filled the workspace. */
+int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void* q, const void* k,
+                     const void* v, float* o, float* lse, int B, int H, int N, int D, int dtype,
+                     double base, const float* alpha, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void* q, const void* k,
+                     const void* v, const float* o, const void* dO, const float* lse, float* dq,
+                     float* dk, float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
+                     double base, const float* alpha, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* rope_attn_status_string(int status);
 

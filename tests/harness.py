@@ -14,29 +14,42 @@ def to_device(x: np.ndarray, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
-def run_gpu(inp: W.Inputs, causal=None, alpha=True, want_dalpha=True):
-    """Forward and backward on the GPU; returns float64 numpy arrays."""
+def run_gpu(inp: W.Inputs, causal=None, alpha=True, want_dalpha=True, opts=None):
+    """Forward and backward on the GPU; returns float64 numpy arrays.  opts:
+    a dict of frequency-schedule options (unrotated_pairs, scale, pos_offset)."""
     import torch
     from bwd_rope_apply_amd import fwd, bwd
     wl = inp.wl
     causal = wl.causal if causal is None else causal
     q, k, v, do = (to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
     a = to_device(inp.alpha) if alpha else None
-    o, lse = fwd(q, k, v, wl.base, a, causal)
-    dq, dk, dv, da = bwd(q, k, v, o, do, lse, wl.base, a, causal, want_dalpha=want_dalpha)
+    o, lse = fwd(q, k, v, wl.base, a, causal, opts=opts)
+    dq, dk, dv, da = bwd(q, k, v, o, do, lse, wl.base, a, causal, want_dalpha=want_dalpha, opts=opts)
     torch.cuda.synchronize()
     out = dict(O=o, LSE=lse, dQ=dq, dK=dk, dV=dv, dalpha=da)
     return {n: (None if t is None else t.double().cpu().numpy()) for n, t in out.items()}
 
 
-def run_oracle(inp: W.Inputs, causal=None, alpha=True):
+def oracle_kwargs(D: int, opts=None) -> dict:
+    """The oracle's arguments for the library's frequency-schedule options."""
+    opts = opts or {}
+    kw = dict(p0=float(opts.get("pos_offset", 0)))
+    if opts.get("unrotated_pairs"):
+        kw["rot"] = D // 2 - opts["unrotated_pairs"]
+    if opts.get("scale"):
+        kw["scale"] = float(np.float32(opts["scale"]))
+    return kw
+
+
+def run_oracle(inp: W.Inputs, causal=None, alpha=True, opts=None):
     from oracle import ref
     wl = inp.wl
     causal = wl.causal if causal is None else causal
     q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
     a = inp.alpha if alpha else None
-    o, lse = ref.ref_fwd(q, k, v, wl.base, a, causal)
-    dq, dk, dv, da = ref.ref_bwd(q, k, v, o, do, lse, wl.base, a, causal)
+    kw = oracle_kwargs(wl.D, opts)
+    o, lse = ref.ref_fwd(q, k, v, wl.base, a, causal, **kw)
+    dq, dk, dv, da = ref.ref_bwd(q, k, v, o, do, lse, wl.base, a, causal, **kw)
     return dict(O=o, LSE=lse, dQ=dq, dK=dk, dV=dv, dalpha=da)
 
 

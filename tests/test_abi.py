@@ -26,8 +26,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["rope_attn_bwd", "rope_attn_bwd_stages", "rope_attn_bwd_workspace_bytes",
-                           "rope_attn_fwd", "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
+    assert _declared() == ["rope_attn_bwd", "rope_attn_bwd_ex", "rope_attn_bwd_stages",
+                           "rope_attn_bwd_workspace_bytes", "rope_attn_fwd", "rope_attn_fwd_ex",
+                           "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
                            "rope_attn_status_string"]
 
 
@@ -61,6 +62,22 @@ A = 4096  # any 16-byte aligned non-null value; validation fails before use
 ])
 def test_fwd_validation(lib, args, status):
     assert lib.rope_attn_fwd(*args) == status
+
+
+@pytest.mark.parametrize("fields,status", [
+    ((-1, 0.0, 0), -7), ((33, 0.0, 0), -7), ((0, -0.5, 0), -7), ((0, float("inf"), 0), -7),
+    ((0, float("nan"), 0), -7), ((0, 0.0, -3), -7), ((0, 0.0, (1 << 30) - 8), -7),
+])
+def test_options_validation(lib, fields, status):
+    """Invalid frequency-schedule options are rejected before any launch
+    (D = 64: unrotated_pairs in [0, 32]; N = 16)."""
+    import ctypes
+    from bwd_rope_apply_amd import _lib
+    op = _lib.Options(*fields)
+    args = (A, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, A, 1 << 30, None)
+    assert lib.rope_attn_fwd_ex(63, ctypes.addressof(op), *args) == status
+    bargs = [A] * 10 + [1, 1, 16, 64, 1, 1e4, None, 1, A, 1 << 30, None]
+    assert lib.rope_attn_bwd_ex(63, ctypes.addressof(op), *bargs) == status
 
 
 def test_bwd_validation(lib):

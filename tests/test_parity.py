@@ -19,9 +19,9 @@ BF16_TOL = 2e-2
 NAMES = ("O", "dQ", "dK", "dV", "dalpha")
 
 
-def _check(inp, causal=None, alpha=True):
-    got = Hn.run_gpu(inp, causal, alpha)
-    ref = Hn.run_oracle(inp, causal, alpha)
+def _check(inp, causal=None, alpha=True, opts=None):
+    got = Hn.run_gpu(inp, causal, alpha, opts=opts)
+    ref = Hn.run_oracle(inp, causal, alpha, opts=opts)
     for n in NAMES + ("LSE",):
         assert np.isfinite(got[n]).all(), n
     if inp.wl.dtype == "fp32":
@@ -82,6 +82,48 @@ def test_bf16_noncausal(D):
 def test_bf16_standard_rope_alpha_null():
     """alpha = NULL means alpha = 0 (standard RoPE)."""
     _check(W.make_inputs(W.get("long_8k", B=1, H=2, N=400)), alpha=False)
+
+
+# frequency-schedule options: LeRoPE's p-RoPE baseline (slowest 25% of bands
+# unrotated), a softmax scale, a large position offset, and all three
+OPTION_CASES = [
+    ("p_rope", dict(unrotated_pairs=16)),
+    ("no_rotation", dict(unrotated_pairs=64)),
+    ("scale", dict(scale=0.6 / 128 ** 0.5)),
+    ("offset", dict(pos_offset=100000)),
+    ("all", dict(unrotated_pairs=16, scale=0.13, pos_offset=4096)),
+]
+
+
+@pytest.mark.parametrize("case,opts", OPTION_CASES, ids=[c for c, _ in OPTION_CASES])
+def test_bf16_frequency_options(case, opts):
+    """long_8k's distributions at N = 333 with each option, against the
+    oracle at the same options (bf16 bar)."""
+    _check(W.make_inputs(W.get("long_8k", B=1, H=2, N=333)), opts=opts)
+
+
+@pytest.mark.parametrize("case,opts", [("p_rope", dict(unrotated_pairs=8)),
+                                       ("all", dict(unrotated_pairs=4, scale=0.3, pos_offset=777))],
+                         ids=["p_rope", "all"])
+def test_fp32_frequency_options(case, opts):
+    """The exact float32 path with the options (fp32 bar)."""
+    _check(W.make_inputs(W.get("tiny_fp32", B=1, H=2, N=100)), opts=opts)
+
+
+def test_relative_offset_invariance_on_gpu():
+    """Shifting every position by the same amount leaves the outputs (and
+    dalpha, by rotational balance) unchanged: the GPU against itself at
+    offsets 0 and 50000.  The two runs round differently rotated operands to
+    fp16, so each carries its own error (up to ~1e-2 of the RMS against the
+    exact result, see the option tests above); their difference is held to
+    the same 2e-2 bar (the triangle inequality allows 4e-2)."""
+    inp = W.make_inputs(W.get("layer_2k", B=1, H=2, N=500))
+    a = Hn.run_gpu(inp)
+    b = Hn.run_gpu(inp, opts=dict(pos_offset=50000))
+    for n in NAMES:
+        e = Hn.err_rms(b[n], a[n])
+        print(n, e)
+        assert e <= BF16_TOL, (n, e)
 
 
 def test_deterministic_and_overwrites_nan():
