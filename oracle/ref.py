@@ -57,6 +57,16 @@ Frequency-schedule variants (optional arguments, defaults = the above):
           act through per-band alpha offsets and such a scale.
   p0      the position of the first row, shared by queries and keys.
 
+Block-list attention (optional ``blocks``): exact attention restricted, for
+each query block of BLOCK = 128 rows, to its own (diagonal) key block plus a
+given set of other key blocks -- the exact part of Multipole Semantic
+Attention ("Retrieval-augmented approximation": exact attention only for the
+retrieved pairs and the local block diagonal).  ``blocks[b][h][qb]`` is an
+iterable of key-block indices; out-of-range entries are ignored, and under
+the causal mask blocks after the diagonal contribute nothing.  O and LSE are
+over exactly the visible keys, so results over disjoint key sets merge
+through their LSEs.
+
 Inputs are numpy arrays [B, H, N, D] of any float type (upcast exactly to
 float64); alpha is [D/2].
 """
@@ -113,18 +123,39 @@ def wedge(x: np.ndarray, g: np.ndarray) -> np.ndarray:
 
 
 # -------------------------------------------------------------- attention
+BLOCK = 128
+
+
+def block_visible(N: int, sel) -> np.ndarray:
+    """[N, N] bool: key j visible to query i when block(j) is block(i) or in
+    sel[block(i)] (no causal mask applied here)."""
+    nb = (N + BLOCK - 1) // BLOCK
+    vis = np.zeros((nb, nb), dtype=bool)
+    for qb in range(nb):
+        vis[qb, qb] = True
+        for kb in (sel[qb] if qb < len(sel) else ()):
+            if 0 <= kb < nb:
+                vis[qb, kb] = True
+    blk = np.arange(N) // BLOCK
+    return vis[blk[:, None], blk[None, :]]
+
+
 def _key_end(r1: int, N: int, causal: bool) -> int:
     """Keys j < key_end can be unmasked for query rows < r1."""
     return r1 if causal else N
 
 
-def _scores(qt_blk, kt, scale, r0, causal):
-    """S = scale * Q~ K~^T for query rows r0.., masked to -inf where j > i."""
+def _scores(qt_blk, kt, scale, r0, causal, vis=None):
+    """S = scale * Q~ K~^T for query rows r0.., masked to -inf where j > i
+    (and, with a block-visibility matrix, where the key's block is not
+    visible to the query's)."""
     S = scale * (qt_blk @ kt.T)
     if causal:
         i = np.arange(r0, r0 + qt_blk.shape[0])[:, None]
         j = np.arange(kt.shape[0])[None, :]
         S = np.where(j <= i, S, -np.inf)
+    if vis is not None:
+        S = np.where(vis[r0:r0 + qt_blk.shape[0], :kt.shape[0]], S, -np.inf)
     return S
 
 
@@ -143,7 +174,7 @@ def _scale(D, scale):
     return 1.0 / np.sqrt(D) if scale is None else float(scale)
 
 
-def _head_fwd(q, k, v, th, causal, p0, block, scale=None):
+def _head_fwd(q, k, v, th, causal, p0, block, scale=None, vis=None):
     N, D = q.shape
     scale = _scale(D, scale)
     phi = angles(N, th, p0)
@@ -153,7 +184,7 @@ def _head_fwd(q, k, v, th, causal, p0, block, scale=None):
     for r0 in range(0, N, block):
         r1 = min(N, r0 + block)
         ke = _key_end(r1, N, causal)
-        S = _scores(qt[r0:r1], kt[:ke], scale, r0, causal)
+        S = _scores(qt[r0:r1], kt[:ke], scale, r0, causal, vis)
         L = _logsumexp(S)
         P = np.exp(S - L[:, None])
         o[r0:r1] = P @ v[:ke]
@@ -161,7 +192,7 @@ def _head_fwd(q, k, v, th, causal, p0, block, scale=None):
     return o, lse
 
 
-def _head_bwd(q, k, v, o, do, lse, th, causal, p0, block, scale=None):
+def _head_bwd(q, k, v, o, do, lse, th, causal, p0, block, scale=None, vis=None):
     N, D = q.shape
     scale = _scale(D, scale)
     phi = angles(N, th, p0)
@@ -173,7 +204,7 @@ def _head_bwd(q, k, v, o, do, lse, th, causal, p0, block, scale=None):
     for r0 in range(0, N, block):
         r1 = min(N, r0 + block)
         ke = _key_end(r1, N, causal)
-        S = _scores(qt[r0:r1], kt[:ke], scale, r0, causal)
+        S = _scores(qt[r0:r1], kt[:ke], scale, r0, causal, vis)
         P = np.exp(S - lse[r0:r1, None])
         dv[:ke] += P.T @ do[r0:r1]
         dP = do[r0:r1] @ v[:ke].T
@@ -198,7 +229,12 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def ref_fwd(q, k, v, base, alpha=None, causal=True, p0=0.0, block=512, scale=None, rot=None):
+def _vis(blocks, b, h, N):
+    return None if blocks is None else block_visible(N, blocks[b][h])
+
+
+def ref_fwd(q, k, v, base, alpha=None, causal=True, p0=0.0, block=512, scale=None, rot=None,
+            blocks=None):
     """Returns (O [B,H,N,D], LSE [B,H,N]), float64; LSE is the natural-log
     log-sum-exp of the scaled, masked scores of each row."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -208,12 +244,13 @@ def ref_fwd(q, k, v, base, alpha=None, causal=True, p0=0.0, block=512, scale=Non
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):  # heads are independent work units
-            o[b, h], lse[b, h] = _head_fwd(q[b, h], k[b, h], v[b, h], th, causal, p0, block, scale)
+            o[b, h], lse[b, h] = _head_fwd(q[b, h], k[b, h], v[b, h], th, causal, p0, block, scale,
+                                           _vis(blocks, b, h, N))
     return o, lse
 
 
 def ref_bwd(q, k, v, o, do, lse, base, alpha=None, causal=True, p0=0.0, block=512, scale=None,
-            rot=None):
+            rot=None, blocks=None):
     """Returns (dQ, dK, dV [B,H,N,D] in the un-rotated frame, dalpha [D/2]):
     the vector-Jacobian product of (Q, K, V, alpha) -> O for the upstream
     gradient dO, given the forward's O and LSE."""
@@ -227,7 +264,7 @@ def ref_bwd(q, k, v, o, do, lse, base, alpha=None, causal=True, p0=0.0, block=51
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = _head_bwd(
                 q[b, h], k[b, h], v[b, h], o[b, h], do[b, h], lse[b, h], th, causal, p0, block,
-                scale)
+                scale, _vis(blocks, b, h, N))
     return dq, dk, dv, dalpha_chain(q, k, dq, dk, th, p0)
 
 

@@ -348,6 +348,109 @@ def test_scale_is_query_scaling():
         assert rel(x, y) < 1e-12
 
 
+# ------------------------------------------------------------ block lists
+def _random_blocks(rng, B, H, nb, causal, p=0.4):
+    out = []
+    for b in range(B):
+        out.append([])
+        for h in range(H):
+            rows = []
+            for qb in range(nb):
+                cand = range(qb) if causal else range(nb)
+                rows.append([kb for kb in cand if kb != qb and rng.random() < p])
+            out[b].append(rows)
+    return out
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_list_all_blocks_is_dense(causal):
+    """Listing every block reproduces causal (or full) attention exactly."""
+    B, H, N, D = 1, 2, 300, 8
+    q, k, v, do = rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D)
+    nb = 3
+    allb = [[[list(range(nb)) for _ in range(nb)] for _ in range(H)] for _ in range(B)]
+    o1, l1 = ref.ref_fwd(q, k, v, 100.0, None, causal, block=50, blocks=allb)
+    o2, l2 = ref.ref_fwd(q, k, v, 100.0, None, causal, block=50)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_list_brute_force(causal):
+    """Per query row, a plain softmax over exactly the keys of its visible
+    blocks (own block, listed blocks, causal mask), with the rotation in its
+    textbook complex form, element by element in Python loops."""
+    B, H, N, D, base = 1, 1, 300, 4, 50.0
+    rng = np.random.default_rng(7 + causal)
+    q, k, v = (rng.normal(size=(B, H, N, D)) for _ in range(3))
+    a = rng.normal(0, 0.3, size=D // 2)
+    blocks = _random_blocks(rng, B, H, 3, causal, p=0.5)
+    o, lse = ref.ref_fwd(q, k, v, base, a, causal, block=64, blocks=blocks)
+    th = np.exp(a) * base ** (-2.0 * np.arange(D // 2) / D)
+    zq = (q[0, 0, :, 0::2] + 1j * q[0, 0, :, 1::2]) * np.exp(1j * np.arange(N)[:, None] * th)
+    zk = (k[0, 0, :, 0::2] + 1j * k[0, 0, :, 1::2]) * np.exp(1j * np.arange(N)[:, None] * th)
+    sel = blocks[0][0]
+    for i in range(0, N, 7):
+        qb = i // 128
+        keys = [j for j in range(N) if (j // 128 == qb or j // 128 in sel[qb]) and (not causal or j <= i)]
+        s = np.array([np.real(np.sum(zq[i] * np.conj(zk[j]))) / math.sqrt(D) for j in keys])
+        mx = s.max()
+        w = np.exp(s - mx)
+        want_lse = mx + math.log(w.sum())
+        want_o = (w[:, None] * v[0, 0, keys]).sum(axis=0) / w.sum()
+        assert abs(lse[0, 0, i] - want_lse) < 1e-12
+        assert np.abs(o[0, 0, i] - want_o).max() < 1e-12
+
+
+def test_block_list_lse_merge():
+    """Inclusion-exclusion over key sets: with S0 = {own}, S1 = S0 + {b1},
+    S2 = S0 + {b2}, S3 = S0 + {b1, b2}: e^L3 = e^L1 + e^L2 - e^L0 and
+    e^L3 O3 = e^L1 O1 + e^L2 O2 - e^L0 O0 (non-causal, query block 2)."""
+    B, H, N, D = 1, 1, 384, 8
+    q, k, v = rnd(B, H, N, D, scale=0.5), rnd(B, H, N, D, scale=0.5), rnd(B, H, N, D)
+    res = {}
+    for name, extra in (("0", []), ("1", [0]), ("2", [1]), ("3", [0, 1])):
+        bl = [[[[], [], extra]]]
+        res[name] = ref.ref_fwd(q, k, v, 100.0, None, False, block=64, blocks=bl)
+    rows = slice(256, 384)
+    e = {n: np.exp(res[n][1][0, 0, rows])[:, None] for n in res}
+    o = {n: res[n][0][0, 0, rows] for n in res}
+    assert rel(e["3"], e["1"] + e["2"] - e["0"]) < 1e-12
+    assert rel(e["3"] * o["3"], e["1"] * o["1"] + e["2"] * o["2"] - e["0"] * o["0"]) < 1e-11
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_list_finite_differences(causal):
+    """Central differences of sum(O * dO) for Q, K, V and alpha under a
+    sparse block pattern (N = 260: three blocks, ragged)."""
+    B, H, N, D, h, base = 1, 1, 260, 4, 1e-6, 30.0
+    rng = np.random.default_rng(11 + causal)
+    q, k, v, do = (rng.normal(size=(B, H, N, D)) for _ in range(4))
+    a = rng.normal(0, 0.3, size=D // 2)
+    bl = [[[[], [0], [1]] if causal else [[2], [], [0, 1]]]]
+    o, l = ref.ref_fwd(q, k, v, base, a, causal, block=100, blocks=bl)
+    g = ref.ref_bwd(q, k, v, o, do, l, base, a, causal, block=100, blocks=bl)
+
+    def L():
+        return float((ref.ref_fwd(q, k, v, base, a, causal, block=100, blocks=bl)[0] * do).sum())
+    for gi, x in enumerate((q, k, v)):
+        for idx in [(0, 0, i, c) for i in (0, 127, 128, 200, 259) for c in range(D)]:
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = L()
+            x[idx] = x0 - h
+            lm = L()
+            x[idx] = x0
+            assert abs((lp - lm) / (2 * h) - g[gi][idx]) < 1e-7 * max(1.0, abs(g[gi][idx])), (gi, idx)
+    for m in range(D // 2):
+        a0 = a[m]
+        a[m] = a0 + h
+        lp = L()
+        a[m] = a0 - h
+        lm = L()
+        a[m] = a0
+        assert abs((lp - lm) / (2 * h) - g[3][m]) < 1e-7 * max(1.0, abs(g[3][m]))
+
+
 # ---------------------------------------------------- finite differences
 FD_CASES = [
     (1, 4, 10.0, True, None, None), (2, 8, 1e4, True, None, None), (5, 4, 10.0, True, None, None),

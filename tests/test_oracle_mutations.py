@@ -28,6 +28,10 @@ PIN_SET = [
     ("variants_autograd", lambda: pins.test_autograd_frequency_variants(0.3, 5, 7.0)),
     ("scale_is_query_scaling", pins.test_scale_is_query_scaling),
     ("fd_variant", lambda: pins.test_finite_differences_all_gradients(5, 8, 1e4, True, 0.21, 3)),
+    ("blocks_dense", lambda: pins.test_block_list_all_blocks_is_dense(True)),
+    ("blocks_brute", lambda: pins.test_block_list_brute_force(True)),
+    ("blocks_merge", pins.test_block_list_lse_merge),
+    ("blocks_fd", lambda: pins.test_block_list_finite_differences(True)),
 ]
 
 
@@ -70,12 +74,14 @@ def _mut_dalpha_keys_only(q, k, dq, dk, th, p0=0.0):
     return _orig_dalpha(q, k, np.zeros_like(dq), dk, th, p0)
 
 
-def _mut_scores_strict_mask(qt_blk, kt, scale, r0, causal):
+def _mut_scores_strict_mask(qt_blk, kt, scale, r0, causal, vis=None):
     S = scale * (qt_blk @ kt.T)
     if causal:
         i = np.arange(r0, r0 + qt_blk.shape[0])[:, None]
         j = np.arange(kt.shape[0])[None, :]
         S = np.where(j < i, S, -np.inf)
+    if vis is not None:
+        S = np.where(vis[r0:r0 + qt_blk.shape[0], :kt.shape[0]], S, -np.inf)
     return S
 
 
@@ -91,6 +97,31 @@ def _mut_theta_hat_rot_off_by_one(base, alpha, D, rot=None):
     return _orig_theta_hat(base, alpha, D, None if rot is None else rot + 1)
 
 
+def _mut_block_visible_64(N, sel):
+    old = ref.BLOCK
+    try:
+        ref.BLOCK = 64
+        return _orig_block_visible(N, sel)
+    finally:
+        ref.BLOCK = old
+
+
+def _mut_block_visible_no_diagonal(N, sel):
+    nb = (N + ref.BLOCK - 1) // ref.BLOCK
+    vis = np.zeros((nb, nb), dtype=bool)
+    for qb in range(nb):
+        for kb in (sel[qb] if qb < len(sel) else ()):
+            if 0 <= kb < nb:
+                vis[qb, kb] = True
+    blk = np.arange(N) // ref.BLOCK
+    return vis[blk[:, None], blk[None, :]]
+
+
+def _mut_head_bwd_ignores_blocks(q, k, v, o, do, lse, th, causal, p0, block, scale=None, vis=None):
+    return _orig_head_bwd(q, k, v, o, do, lse, th, causal, p0, block, scale, None)
+
+
+_orig_block_visible = ref.block_visible
 _orig_theta_hat = ref.theta_hat
 _orig_dalpha = ref.dalpha_chain
 _orig_head_bwd = ref._head_bwd
@@ -98,7 +129,7 @@ _orig_head_bwd = ref._head_bwd
 
 def _mut_head_bwd(variant):
     """A copy of the per-head backward with one planted mistake."""
-    def f(q, k, v, o, do, lse, th, causal, p0, block, scale=None):
+    def f(q, k, v, o, do, lse, th, causal, p0, block, scale=None, vis=None):
         N, D = q.shape
         scale = ref._scale(D, scale)
         if variant == "dk_default_scale":
@@ -112,7 +143,7 @@ def _mut_head_bwd(variant):
         for r0 in range(0, N, block):
             r1 = min(N, r0 + block)
             ke = r1 if causal else N
-            S = ref._scores(qt[r0:r1], kt[:ke], scale, r0, causal)
+            S = ref._scores(qt[r0:r1], kt[:ke], scale, r0, causal, vis)
             P = np.exp(S - lse[r0:r1, None])
             if variant == "dv_transposed":
                 dv[:ke] += P @ do[:ke] if P.shape[0] == P.shape[1] else P.T @ do[r0:r1]
@@ -150,6 +181,9 @@ MUTANTS = {
     "dk_ignores_scale_argument": ("_head_bwd", _mut_head_bwd("dk_default_scale")),
     "partial_rope_ignored": ("theta_hat", _mut_theta_hat_ignores_rot),
     "partial_rope_one_band_too_many": ("theta_hat", _mut_theta_hat_rot_off_by_one),
+    "blocks_of_64_rows": ("block_visible", _mut_block_visible_64),
+    "blocks_without_own_block": ("block_visible", _mut_block_visible_no_diagonal),
+    "backward_ignores_blocks": ("_head_bwd", _mut_head_bwd_ignores_blocks),
 }
 
 
