@@ -16,6 +16,10 @@ staged entry points, so the timed work is exactly the full forward +
 backward.  One workspace serves both passes: the backward reuses the
 forward's rotated fp16 planes and frequency table (saved activations) and
 prepares only dO and D.
+
+--retrieved K times block-list attention instead (each 128-row query block
+sees its own block and K seeded key blocks, the exact part of Multipole
+Semantic Attention); flops then count the visible pairs only.
 """
 from __future__ import annotations
 
@@ -54,6 +58,9 @@ def parse():
                     help="frequency-schedule option: softmax scale (0 = 1/sqrt(D))")
     ap.add_argument("--pos-offset", type=int, default=0,
                     help="frequency-schedule option: position of row 0")
+    ap.add_argument("--retrieved", type=int, default=-1,
+                    help="block-list attention: key blocks retrieved per 128-row query block "
+                         "(seeded, uniform among the blocks it may see); -1 = dense")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_8k.json"),
                     help="JSON with measured HBM bytes per launch of the MFMA kernels (used only "
                          "if it was taken on the current kernel source)")
@@ -109,6 +116,25 @@ def cpu_baseline(inp, wl):
                       f"dalpha, {dt:.1f} s"}
 
 
+def visible_pairs(lists, N: int, causal: bool) -> int:
+    """(query, key) pairs that block lists leave visible: per query block
+    its own block (the causal triangle under the mask) and each distinct
+    listed block in range (earlier blocks only under the mask)."""
+    nb = (N + 127) // 128
+    size = [min(128, N - 128 * b) for b in range(nb)]
+    total = 0
+    for per_b in lists:
+        for per_h in per_b:
+            for qb, sel in enumerate(per_h):
+                seen = {qb} | {kb for kb in sel if 0 <= kb < nb and (not causal or kb <= qb)}
+                for kb in seen:
+                    if causal and kb == qb:
+                        total += size[qb] * (size[qb] + 1) // 2
+                    else:
+                        total += size[qb] * size[kb]
+    return total
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,6 +174,18 @@ def main():
     if args.unrotated_pairs or args.scale or args.pos_offset:
         opts = dict(unrotated_pairs=args.unrotated_pairs, scale=args.scale,
                     pos_offset=args.pos_offset)
+    opts_config = dict(opts) if opts else None
+    # algorithmic flops: 12 D per visible (query, key) pair (forward QK^T and
+    # PV, backward dQ, dV, dP, dK); dense causal attention counts N^2 / 2
+    # pairs per head
+    pairs = B * H * N * N / 2.0
+    if args.retrieved >= 0:
+        lists = W.block_lists(B, H, N, args.retrieved, wl.causal, wl.seed)
+        opts = dict(opts or {}, blocks=_lib.block_csr(lists, dev))
+        pairs = float(visible_pairs(lists, N, wl.causal))
+        opts_config = dict(opts_config or {}, block_lists={
+            "retrieved": args.retrieved, "block": 128,
+            "density_vs_causal": round(pairs / (B * H * N * (N + 1) / 2.0), 4)})
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -196,14 +234,14 @@ def main():
     fwd_ev = np.array([ev[s][0].elapsed_time(ev[s][nf]) for s in range(args.steps)])
     bwd_ev = np.array([ev[s][nf].elapsed_time(ev[s][len(names)]) for s in range(args.steps)])
     ms_step = wall * 1e3 / args.steps
-    unit = float(B) * H * N * N * D
+    unit = 2.0 * pairs * D
     flops = 6.0 * unit
     value = flops / (ms_step * 1e-3) / 1e12
 
     dom = max(STAGE_FLOP_UNITS, key=lambda n: stage_ms[n])
     dom_flops = STAGE_FLOP_UNITS[dom] * unit
     achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
-    traffic = measured_traffic(args.traffic, dom)
+    traffic = measured_traffic(args.traffic, dom) if args.retrieved < 0 else None
     kernel = {"fwd_main": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}[dom]
     line = {
         "metric": METRIC,
@@ -220,7 +258,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
                    "base": wl.base, "storage": wl.dtype, "outputs": "fp32",
-                   "options": opts,
+                   "options": opts_config,
                    "flops_per_step": flops, "pct_bf16_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),

@@ -29,16 +29,44 @@ _lib = None
 class Options(ctypes.Structure):
     """rope_attn_options: unrotated_pairs (the slowest bands left unrotated,
     partial RoPE), scale (softmax scale, 0 = 1/sqrt(D)), pos_offset (position
-    of row 0)."""
+    of row 0), and block lists (device int32 CSR pointers over the B*H*nb
+    query blocks of 128 rows, and the number of entries)."""
     _fields_ = [("unrotated_pairs", ctypes.c_int), ("scale", ctypes.c_float),
-                ("pos_offset", ctypes.c_int)]
+                ("pos_offset", ctypes.c_int), ("block_ptr", ctypes.c_void_p),
+                ("block_idx", ctypes.c_void_p), ("block_nnz", ctypes.c_int)]
 
 
 def _opts(opts):
-    """None, an Options, or a dict with any of its fields."""
+    """None, an Options, or a dict with any of its fields; a dict may give
+    ``blocks`` = (ptr, idx) int32 device tensors instead of the raw fields."""
     if opts is None or isinstance(opts, Options):
         return opts
+    opts = dict(opts)
+    blocks = opts.pop("blocks", None)
+    if blocks is not None:
+        import torch
+        ptr, idx = blocks
+        for name, t in (("ptr", ptr), ("idx", idx)):
+            if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"block {name} must be a contiguous int32 device tensor")
+        opts["block_ptr"] = ptr.data_ptr()
+        opts["block_idx"] = idx.data_ptr() if idx.numel() else None
+        opts["block_nnz"] = int(idx.numel())
     return Options(**opts)
+
+
+def block_csr(lists, device=None):
+    """CSR (ptr, idx) int32 tensors from nested lists ``lists[b][h][qb]`` of
+    key-block indices (every query block of every head, in order)."""
+    import torch
+    ptr, idx = [0], []
+    for per_b in lists:
+        for per_h in per_b:
+            for sel in per_h:
+                idx.extend(int(x) for x in sel)
+                ptr.append(len(idx))
+    mk = lambda a: torch.tensor(a, dtype=torch.int32, device=device)
+    return mk(ptr), mk(idx)
 
 
 class RopeAttnError(RuntimeError):

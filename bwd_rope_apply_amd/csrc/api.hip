@@ -16,11 +16,15 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Shape {
   int B, H, N, D, dtype, causal;
+  int blocks;  // block-list attention requested
   size_t bh() const { return (size_t)B * H; }
   size_t elems() const { return bh() * N * D; }
   bool bf16() const { return dtype == ROPE_ATTN_BF16; }
-  // split-operand corner rows: bf16 causal only
-  int corner() const { return (bf16() && causal) ? corner_rows(N) : 0; }
+  // split-operand corner rows: bf16 causal only.  With block lists every row
+  // averages at most its listed blocks, so the first block suffices.
+  int corner() const { return (bf16() && causal) ? (blocks ? BLK : corner_rows(N)) : 0; }
+  // block visibility bitmask (any call that may use block lists)
+  bool mask_ok() const { return N <= MAX_BLOCKS * BLK; }
 };
 
 int check_shape(const Shape& s) {
@@ -36,18 +40,34 @@ int check_shape(const Shape& s) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
-// Frequency-schedule options with their defaults resolved.
+bool misaligned_4(const void* p) { return ((uintptr_t)p & 3u) != 0; }
+
+// Options with their defaults resolved.
 struct Opts {
   int rot;      // rotated bands (D/2 - unrotated_pairs)
   float scale;  // softmax scale
   int pos0;     // position of row 0
+  const int* bptr;  // block lists (CSR over BH x n_blocks query blocks), or null
+  const int* bidx;
+  int bnnz;
 };
 
 int resolve(const rope_attn_options* o, const Shape& s, Opts& r) {
   r.rot = s.D / 2;
   r.scale = 1.0f / sqrtf((float)s.D);
   r.pos0 = 0;
+  r.bptr = nullptr;
+  r.bidx = nullptr;
+  r.bnnz = 0;
   if (!o) return ROPE_ATTN_OK;
+  if (o->block_ptr) {
+    if (!s.mask_ok()) return ROPE_ATTN_ERR_SHAPE;
+    if (o->block_nnz < 0 || (o->block_nnz > 0 && !o->block_idx)) return ROPE_ATTN_ERR_ARG;
+    if (misaligned_4(o->block_ptr) || misaligned_4(o->block_idx)) return ROPE_ATTN_ERR_ALIGN;
+    r.bptr = o->block_ptr;
+    r.bidx = o->block_idx;
+    r.bnnz = o->block_nnz;
+  }
   if (o->unrotated_pairs < 0 || o->unrotated_pairs > s.D / 2) return ROPE_ATTN_ERR_ARG;
   if (!(o->scale == 0.0f || (isfinite(o->scale) && o->scale > 0.0f))) return ROPE_ATTN_ERR_ARG;
   if (o->pos_offset < 0 || (long)o->pos_offset + s.N > (1L << 30)) return ROPE_ATTN_ERR_ARG;
@@ -62,10 +82,10 @@ int resolve(const rope_attn_options* o, const Shape& s, Opts& r) {
 // and are laid out identically by both passes, so a backward run on the
 // forward's workspace can reuse them (ROPE_ATTN_STAGE_PREP_GRAD).
 struct Layout {
-  size_t theta, cs, qh, kh, vh, qlo, klo, doh, drow, rs, dkp, dvp, part;
+  size_t theta, cs, qh, kh, vh, qlo, klo, bmask, doh, drow, rs, dkp, dvp, part;
   int slots;
   size_t total() const {
-    return theta + cs + qh + kh + vh + qlo + klo + doh + drow + rs + dkp + dvp + part;
+    return theta + cs + qh + kh + vh + qlo + klo + bmask + doh + drow + rs + dkp + dvp + part;
   }
 };
 
@@ -79,8 +99,18 @@ MfmaParams mfma_base(const Shape& s, float scale) {
   return m;
 }
 
-Layout layout(const Shape& s, bool bwd) {
+// dQ/dK/dV/dalpha partial-sum slots of the MFMA path for one corner choice
+int mfma_slots(const Shape& s) {
+  const MfmaParams m = mfma_base(s, 1.0f);
+  return (s.corner() ? corner_dq_slots(m) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
+}
+
+// Region sizes do not depend on whether a call passes block lists (the
+// workspace queries take no options): corner regions are sized for the
+// larger, dense corner, and the slot count is the larger of the two.
+Layout layout(Shape s, bool bwd) {
   Layout L = {};
+  s.blocks = 0;
   L.theta = up(sizeof(double) * (s.D / 2));
   L.cs = up(sizeof(float2) * (size_t)s.N * (s.D / 2));
   const size_t h16 = up(2 * s.elems());
@@ -89,13 +119,16 @@ Layout layout(const Shape& s, bool bwd) {
     if (bwd) L.doh = h16;
     if (s.corner()) L.qlo = L.klo = up(2 * s.bh() * s.corner() * s.D);
   }
+  if (s.mask_ok()) L.bmask = up(sizeof(uint32_t) * s.bh() * n_blocks(s.N) * mask_words(s.N));
   if (bwd) {
     L.drow = up(sizeof(float) * s.bh() * s.N);
     if (s.bf16()) L.rs = up(sizeof(float) * s.bh() * rs_groups(s.N) * 64);
     if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * s.corner() * s.D);
     if (s.bf16()) {
-      const MfmaParams m = mfma_base(s, 1.0f);
-      L.slots = (s.corner() ? corner_dq_slots(m) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
+      Shape sb = s;
+      sb.blocks = 1;
+      L.slots = mfma_slots(s);
+      if (s.mask_ok()) L.slots = max(L.slots, mfma_slots(sb));
     } else {
       L.slots = 2 * simt_slots((int)s.bh(), s.N);
     }
@@ -133,6 +166,20 @@ void tables(const Shape& s, const Opts& op, double base, const float* alpha, dou
   launch_table(t, st);
 }
 
+void block_mask(const Shape& s, const Opts& op, uint32_t* mask, hipStream_t st) {
+  BlockMaskParams bp = {};
+  bp.ptr = op.bptr; bp.idx = op.bidx; bp.nnz = op.bnnz; bp.mask = mask;
+  bp.nb = n_blocks(s.N); bp.W = mask_words(s.N); bp.rows = (int)s.bh() * bp.nb;
+  bp.causal = s.causal;
+  launch_block_mask(bp, st);
+}
+
+void set_blocks(MfmaParams& m, const Shape& s, const Opts& op, const uint32_t* mask) {
+  m.bmask = op.bptr ? mask : nullptr;
+  m.nb = n_blocks(s.N);
+  m.W = mask_words(s.N);
+}
+
 int finish() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? ROPE_ATTN_OK : ROPE_ATTN_ERR_HIP;
@@ -158,15 +205,18 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
                      const void* v, float* o, float* lse, int B, int H, int N, int D, int dtype,
                      double base, const float* alpha, int causal, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  const Shape s{B, H, N, D, dtype, causal};
+  Shape s{B, H, N, D, dtype, causal, 0};
   if (!q || !k || !v || !o || !lse) return ROPE_ATTN_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
       misaligned(alpha))
     return ROPE_ATTN_ERR_ALIGN;
-  int st = check_common(s, base, workspace, workspace_bytes, false);
+  int st = check_shape(s);
   if (st) return st;
   Opts op;
   st = resolve(opts, s, op);
+  if (st) return st;
+  s.blocks = op.bptr != nullptr;
+  st = check_common(s, base, workspace, workspace_bytes, false);
   if (st) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -179,9 +229,11 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   half_t* vh = c.take<half_t>(L.vh);
   half_t* qlo = c.take<half_t>(L.qlo);
   half_t* klo = c.take<half_t>(L.klo);
+  uint32_t* bmask = c.take<uint32_t>(L.bmask);
 
   if (stages & ROPE_ATTN_STAGE_PREP) {
     tables(s, op, base, alpha, theta, cs, hs);
+    if (op.bptr) block_mask(s, op, bmask, hs);
     if (s.bf16()) {
       PrepParams pp = {};
       pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
@@ -193,6 +245,7 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   }
   MfmaParams mp = mfma_base(s, op.scale);
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.qlo = qlo; mp.klo = klo; mp.o = o; mp.out_lse = lse;
+  set_blocks(mp, s, op, bmask);
   if (stages & ROPE_ATTN_STAGE_EXACT) {
     if (!s.bf16()) {
       SimtParams sp = {};
@@ -200,6 +253,7 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       sp.bf16 = 0; sp.BH = (int)s.bh(); sp.N = N; sp.D = D; sp.causal = causal;
       sp.scale = op.scale;
       sp.rows = N;
+      sp.bmask = mp.bmask; sp.nb = mp.nb; sp.W = mp.W;
       launch_simt_fwd(sp, hs);
     } else if (s.corner()) {
       launch_corner_fwd(mp, hs);
@@ -229,16 +283,19 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
                      float* dk, float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
                      double base, const float* alpha, int causal, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  const Shape s{B, H, N, D, dtype, causal};
+  Shape s{B, H, N, D, dtype, causal, 0};
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ROPE_ATTN_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dO) ||
       misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(alpha) ||
       misaligned(dalpha))
     return ROPE_ATTN_ERR_ALIGN;
-  int st = check_common(s, base, workspace, workspace_bytes, true);
+  int st = check_shape(s);
   if (st) return st;
   Opts op;
   st = resolve(opts, s, op);
+  if (st) return st;
+  s.blocks = op.bptr != nullptr;
+  st = check_common(s, base, workspace, workspace_bytes, true);
   if (st) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -251,6 +308,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   half_t* vh = c.take<half_t>(L.vh);
   half_t* qlo = c.take<half_t>(L.qlo);
   half_t* klo = c.take<half_t>(L.klo);
+  uint32_t* bmask = c.take<uint32_t>(L.bmask);
   half_t* doh = c.take<half_t>(L.doh);
   float* drow = c.take<float>(L.drow);
   float* rs = c.take<float>(L.rs);
@@ -270,6 +328,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
     // PREP_GRAD alone: the table and the Q~, K~, V planes are the forward's
     const bool full = (stages & ROPE_ATTN_STAGE_PREP) != 0;
     if (full) tables(s, op, base, alpha, theta, cs, hs);
+    if (full && op.bptr) block_mask(s, op, bmask, hs);
     PrepParams pp = {};
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
     pp.qh = full ? qh : nullptr; pp.kh = full ? kh : nullptr; pp.vh = full ? vh : nullptr;
@@ -282,6 +341,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   }
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.qlo = qlo; mp.klo = klo; mp.q = q; mp.k = k;
   mp.cs = cs; mp.lse = lse; mp.drow = drow; mp.rs = rs; mp.dq = dq; mp.dk = dk; mp.dv = dv;
+  set_blocks(mp, s, op, bmask);
   mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
   if (stages & ROPE_ATTN_STAGE_EXACT) {
     if (!s.bf16()) {
@@ -291,6 +351,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       sp.bf16 = 0; sp.BH = BHi; sp.N = N; sp.D = D; sp.causal = causal;
       sp.scale = op.scale;
       sp.rows = N; sp.qend = N; sp.final_ = 1;
+      sp.bmask = mp.bmask; sp.nb = mp.nb; sp.W = mp.W;
       sp.slot0 = 0;
       launch_simt_dq(sp, hs);
       sp.slot0 = n_exact_dq;

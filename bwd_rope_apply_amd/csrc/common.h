@@ -33,6 +33,15 @@ __host__ __device__ inline int corner_rows(int N) {
 // their P = exp2(S - LSE2) is exactly 0.
 __host__ __device__ inline int rs_groups(int N) { return (N + 31) / 32 + 1; }
 
+// Block-list attention: query and key blocks of BLK rows; a visibility
+// bitmask row [W words] per (bh, query block), bit kb set when the query
+// block attends key block kb (its own block always).  Up to MAX_BLOCKS
+// blocks per head (N <= 65536).
+constexpr int BLK = 128;
+constexpr int MAX_BLOCKS = 512;
+__host__ __device__ inline int n_blocks(int N) { return (N + BLK - 1) / BLK; }
+__host__ __device__ inline int mask_words(int N) { return (n_blocks(N) + 31) / 32; }
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -62,6 +71,15 @@ struct PrepParams {
   int BH, N, D;
 };
 
+struct BlockMaskParams {
+  const int* ptr;       // [rows + 1] CSR offsets into idx (device)
+  const int* idx;       // [nnz] key-block indices (device)
+  int nnz;
+  uint32_t* mask;       // [rows][W] output
+  int rows, nb, W;      // rows = BH * nb
+  int causal;
+};
+
 // Exact fp32 path (one query or key row per 4-lane group).
 struct SimtParams {
   const void* q; const void* k; const void* v; const void* dO;
@@ -73,6 +91,8 @@ struct SimtParams {
   float* dk_part; float* dv_part;       // [BH][rows][D] rotated-frame partials (final == 0)
   float* dalpha_part;                   // [slots][D/2]
   int slot0;                            // first dalpha slot of this launch
+  const uint32_t* bmask;                // block visibility [BH][nb][W], or null (all visible)
+  int nb, W;
   int bf16;
   int BH, N, D;
   int rows;        // query rows (fwd, dq) or key rows (dkdv) handled: [0, rows)
@@ -95,6 +115,8 @@ struct MfmaParams {
   float* dk_part; float* dv_part;   // corner partials [BH][corner][D] or null
   float* dalpha_part;
   int slot0;
+  const uint32_t* bmask;           // block visibility [BH][nb][W], or null (causal triangle / all)
+  int nb, W;
   int bf16;
   int B, H, N, D;
   int corner;      // rows [0, corner) are done by the corner kernels
@@ -112,6 +134,7 @@ struct DalphaParams {
 // ------------------------------------------------------------------ launchers
 void launch_table(const TableParams& p, hipStream_t s);
 void launch_prep(const PrepParams& p, hipStream_t s);
+void launch_block_mask(const BlockMaskParams& p, hipStream_t s);
 void launch_simt_fwd(const SimtParams& p, hipStream_t s);
 void launch_simt_dq(const SimtParams& p, hipStream_t s);
 void launch_simt_dkdv(const SimtParams& p, hipStream_t s);
@@ -144,6 +167,15 @@ __device__ __forceinline__ void load4(const void* base, size_t idx, int bf16, fl
     float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
     x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
   }
+}
+
+// Whether key `key` is visible to query row `row` under a block mask (null:
+// all blocks visible; the causal mask is separate).
+__device__ __forceinline__ bool block_visible(const uint32_t* bm, int nb, int W, int bh, int row,
+                                              int key) {
+  if (!bm) return true;
+  const int kb = key / BLK;
+  return (bm[((size_t)bh * nb + row / BLK) * W + (kb >> 5)] >> (kb & 31)) & 1u;
 }
 
 // Turn the pair (x0, x1) by +phi given (cos phi, sin phi).

@@ -223,11 +223,13 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
 constexpr int FWD_NB = RA_FWD_NB;
 constexpr int FWD_BM = 4 * 32 * FWD_NB;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, BN>::ALLOC, NB = FWD_NB;
   __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
+  __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the key blocks, ascending
+  __shared__ int bcount;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
@@ -256,32 +258,53 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
     m[nb] = -INFINITY;
     l[nb] = 0.f;
   }
-  const int nk = (p.N + BN - 1) / BN;
-  const int n_kt = CAUSAL ? min(nk, (q0 + FWD_BM + BN - 1) / BN) : nk;
   const int wlast = wrow0 + 32 * NB - 1;
+  // steps before `split` need no mask for any wave (the workgroup's diagonal
+  // and the ragged tail come after); the loop is peeled there so each loop
+  // carries a single inlined tile body.  Block-list mode walks the listed
+  // key blocks (two steps each; the own block, masked, is the last under the
+  // causal mask, and a ragged last block is the last in any case, cut to
+  // the steps that start below N).
+  int n_kt, split;
+  if constexpr (BL) {
+    static_assert(FWD_BM == BLK && BLK == 2 * BN, "one query block per workgroup");
+    if (w == 0) {
+      const int c = row_blocks(p.bmask + ((size_t)bh * p.nb + t) * p.W, p.nb, blist, lane);
+      if (lane == 0) bcount = c;
+    }
+    __syncthreads();
+    const int last = blist[bcount - 1];
+    const int rows = min(BLK, p.N - last * BLK), steps = (rows + BN - 1) / BN;
+    n_kt = 2 * (bcount - 1) + steps;
+    split = ((CAUSAL && last == t) || rows < BLK) ? n_kt - steps : n_kt;
+  } else {
+    const int nk = (p.N + BN - 1) / BN;
+    n_kt = CAUSAL ? min(nk, (q0 + FWD_BM + BN - 1) / BN) : nk;
+    split = min(n_kt, min(CAUSAL ? q0 / BN : nk, p.N / BN));
+  }
+  Walk<BN, BL> walk;
+  walk.init(blist, 0, n_kt);
 
   TileDMA<D, BN> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, 0, p.N);
-  dma.load(Vs, vh, 0, p.N);
+  dma.load(Ks, kh, walk.cur, p.N);
+  dma.load(Vs, vh, walk.cur, p.N);
   wait_lds_copies();
   __syncthreads();
-  // steps before `split` need no mask for any wave (the workgroup's diagonal
-  // and the ragged tail come after); the loop is peeled there so each loop
-  // carries a single inlined tile body
-  const int split = min(n_kt, min(CAUSAL ? q0 / BN : nk, p.N / BN));
   auto step = [&](int kt, auto masked) {
-    const int k0 = kt * BN;
+    const int k0 = walk.cur;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
     if (kt + 1 < n_kt) {
-      dma.load(Ks + nxt, kh, k0 + BN, p.N);
-      dma.load(Vs + nxt, vh, k0 + BN, p.N);
+      dma.load(Ks + nxt, kh, walk.next, p.N);
+      dma.load(Vs + nxt, vh, walk.next, p.N);
     }
+    walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (active && !(CAUSAL && k0 > wlast))  // skip tiles wholly above this wave's rows
       fwd_tile<D, NB, decltype(masked)::value>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, lane);
     wait_lds_copies();
     __syncthreads();
+    walk.advance(kt);
   };
   int kt = 0;
   for (; kt < split; ++kt) step(kt, std::false_type{});
@@ -313,12 +336,14 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
 // Workgroup = 128 query rows; streams KB-key tiles of K~ and V.  The K~
 // tile serves both the score product (natural reads) and dQ~ += dS K~
 // (transposed reads).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
   constexpr int KB = RA_DQ_BN, NMB = KB / 32;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, KB>::ALLOC;
   __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
+  __shared__ short blist[BL ? MAX_BLOCKS : 1];
+  __shared__ int bcount;
   __shared__ float red[4 * (D / 2)];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
@@ -342,32 +367,51 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
   f32x16 acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
-  const int nk = (p.N + KB - 1) / KB;
-  const int n_kt = CAUSAL ? min(nk, (q0 + BM + KB - 1) / KB) : nk;
+  // unmasked steps first, then the diagonal and ragged tail (peeled loops,
+  // one inlined tile body each); block-list mode walks the listed key blocks
+  constexpr int SPB = BLK / KB;   // steps per block
+  int n_kt, split;
+  if constexpr (BL) {
+    static_assert(BM == BLK && BLK % KB == 0, "one query block per workgroup");
+    if (w == 0) {
+      const int c = row_blocks(p.bmask + ((size_t)bh * p.nb + t) * p.W, p.nb, blist, lane);
+      if (lane == 0) bcount = c;
+    }
+    __syncthreads();
+    const int last = blist[bcount - 1];
+    const int rows = min(BLK, p.N - last * BLK), steps = (rows + KB - 1) / KB;
+    n_kt = SPB * (bcount - 1) + steps;
+    split = ((CAUSAL && last == t) || rows < BLK) ? n_kt - steps : n_kt;
+  } else {
+    const int nk = (p.N + KB - 1) / KB;
+    n_kt = CAUSAL ? min(nk, (q0 + BM + KB - 1) / KB) : nk;
+    split = min(n_kt, min(CAUSAL ? q0 / KB : nk, p.N / KB));
+  }
+  Walk<KB, BL> walk;
+  walk.init(blist, 0, n_kt);
 
   TileDMA<D, KB> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, 0, p.N);
-  dma.load(Vs, vh, 0, p.N);
+  dma.load(Ks, kh, walk.cur, p.N);
+  dma.load(Vs, vh, walk.cur, p.N);
   wait_lds_copies();
   __syncthreads();
   const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;
-  // unmasked steps first, then the diagonal and ragged tail (peeled loops,
-  // one inlined tile body each)
-  const int split = min(n_kt, min(CAUSAL ? q0 / KB : nk, p.N / KB));
   auto step = [&](int kt, auto masked) {
-    const int k0 = kt * KB;
+    const int k0 = walk.cur;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
     if (kt + 1 < n_kt) {
-      dma.load(Ks + nxt, kh, k0 + KB, p.N);
-      dma.load(Vs + nxt, vh, k0 + KB, p.N);
+      dma.load(Ks + nxt, kh, walk.next, p.N);
+      dma.load(Vs + nxt, vh, walk.next, p.N);
     }
+    walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (!(CAUSAL && k0 > wrow0 + 31))
       dq_tile<D, NMB, decltype(masked)::value>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, lse2, dr,
                                                lane);
     wait_lds_copies();
     __syncthreads();
+    walk.advance(kt);
   };
   int kt = 0;
   for (; kt < split; ++kt) step(kt, std::false_type{});
@@ -388,7 +432,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
 // tiles of Q~ and dO plus their row scalars.  Q~ serves the score product
 // and dK~ += dS^T Q~; dO serves dP = dO V^T and dV += P^T dO.  The
 // workgroup's V rows stay in LDS (natural layout) and feed dP.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   constexpr int QB = RA_DKDV_BN, NMB = QB / 32;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, QB>::ALLOC;
@@ -397,6 +441,9 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(16))) half_t Vst[BM * (D + 8)];
   __shared__ __attribute__((aligned(16))) float rsl[2 * 2 * QB];
   __shared__ float red[4 * (D / 2)];
+  __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the query blocks, ascending
+  __shared__ uint32_t bcol[BL ? MAX_BLOCKS / 32 : 1];
+  __shared__ int bcount;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
@@ -427,7 +474,25 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   for (int cb = 0; cb < CB; ++cb) { dk[cb] = f32x16{}; dv[cb] = f32x16{}; }
   int qs0 = CAUSAL ? k0 : 0;
   if (qs0 < p.corner) qs0 = p.corner;  // pairs with query rows < corner: exact path
-  const int n_it = qs0 < p.N ? (p.N - qs0 + QB - 1) / QB : 0;
+  // block-list mode: the query blocks that attend this key block (the own
+  // block first, masked, under the causal mask; rows < corner excluded; a
+  // ragged last block cut to the steps that start below N, as the row
+  // scalars end there)
+  constexpr int SPB = BLK / QB;
+  int n_it;
+  if constexpr (BL) {
+    static_assert(BM == BLK && BLK % QB == 0, "one key block per workgroup");
+    const int cnt = column_blocks<256>(p.bmask, p.nb, p.W, bh, t, qs0 / BLK, bcol, blist, &bcount);
+    n_it = 0;
+    if (cnt > 0) {
+      const int rows = min(BLK, p.N - blist[cnt - 1] * BLK);
+      n_it = SPB * (cnt - 1) + (rows + QB - 1) / QB;
+    }
+  } else {
+    n_it = qs0 < p.N ? (p.N - qs0 + QB - 1) / QB : 0;
+  }
+  Walk<QB, BL> walk;
+  walk.init(blist, qs0, n_it);
 
   TileDMA<D, QB> dma;
   dma.init(lane, w);
@@ -439,22 +504,28 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     if (dma.wave < NMB)
       lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane, rsl + buf * 2 * QB + dma.wave * 64);
   };
-  if (n_it > 0) load_rows(qs0, 0);
+  if (n_it > 0) load_rows(walk.cur, 0);
   wait_lds_copies();
   __syncthreads();
   // the first steps cross the workgroup's diagonal (masked), the rest need
   // no mask: peeled loops, one inlined tile body each
-  const int n_masked = (CAUSAL && qs0 <= k0 + BM - 2) ? min(n_it, (k0 + BM - 2 - qs0) / QB + 1) : 0;
+  int n_masked;
+  if constexpr (BL)
+    n_masked = (CAUSAL && n_it > 0 && blist[0] == t) ? min(n_it, SPB) : 0;
+  else
+    n_masked = (CAUSAL && qs0 <= k0 + BM - 2) ? min(n_it, (k0 + BM - 2 - qs0) / QB + 1) : 0;
   auto step = [&](int it, auto masked) {
-    const int r0 = qs0 + it * QB;
+    const int r0 = walk.cur;
     const int cur = it & 1;
-    if (it + 1 < n_it) load_rows(r0 + QB, cur ^ 1);
+    if (it + 1 < n_it) load_rows(walk.next, cur ^ 1);
+    walk.prefetch(it);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (!(CAUSAL && wkey0 > r0 + QB - 1))  // skip tiles wholly before this wave's keys
       dkdv_tile<D, NMB, decltype(masked)::value>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
                                                  rsl + cur * 2 * QB, kf, vrow, r0, key, lane);
     wait_lds_copies();
     __syncthreads();
+    walk.advance(it);
   };
   int it = 0;
   for (; it < n_masked; ++it) step(it, std::true_type{});
@@ -499,16 +570,21 @@ int dkdv_blocks(const MfmaParams& p) { return p.B * p.H * ((p.N + BM - 1) / BM);
 int dq_mfma_slots(const MfmaParams& p) { return fwd_blocks(p); }
 int dkdv_mfma_slots(const MfmaParams& p) { return dkdv_blocks(p); }
 
+#define RA_LAUNCH1(KERNEL, BL)                                                                  \
+  do {                                                                                         \
+    if (p.D == 64) {                                                                           \
+      if (p.causal) hipLaunchKernelGGL((KERNEL<64, true, BL>), grid, block, 0, s, p);          \
+      else hipLaunchKernelGGL((KERNEL<64, false, BL>), grid, block, 0, s, p);                  \
+    } else {                                                                                   \
+      if (p.causal) hipLaunchKernelGGL((KERNEL<128, true, BL>), grid, block, 0, s, p);         \
+      else hipLaunchKernelGGL((KERNEL<128, false, BL>), grid, block, 0, s, p);                 \
+    }                                                                                          \
+  } while (0)
 #define RA_LAUNCH(KERNEL, BLOCKS)                                                               \
   do {                                                                                         \
     const dim3 grid((unsigned)(BLOCKS)), block(256);                                           \
-    if (p.D == 64) {                                                                           \
-      if (p.causal) hipLaunchKernelGGL((KERNEL<64, true>), grid, block, 0, s, p);              \
-      else hipLaunchKernelGGL((KERNEL<64, false>), grid, block, 0, s, p);                      \
-    } else {                                                                                   \
-      if (p.causal) hipLaunchKernelGGL((KERNEL<128, true>), grid, block, 0, s, p);             \
-      else hipLaunchKernelGGL((KERNEL<128, false>), grid, block, 0, s, p);                     \
-    }                                                                                          \
+    if (p.bmask) RA_LAUNCH1(KERNEL, true);                                                     \
+    else RA_LAUNCH1(KERNEL, false);                                                            \
   } while (0)
 
 void launch_fwd_mfma(const MfmaParams& p, hipStream_t s) {

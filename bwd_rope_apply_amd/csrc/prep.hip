@@ -128,6 +128,31 @@ void launch_prep(const PrepParams& p, hipStream_t s) {
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
 }
 
+// Block visibility rows from a CSR list, one wave per (bh, query block):
+// lanes take the list's entries in turn and OR their bits into an LDS row;
+// the own block always; entries out of range are skipped and duplicates
+// merge; under the causal mask no block after the own one.  Offsets are
+// clamped to [0, nnz], so no read leaves the list.
+__global__ __launch_bounds__(64) void block_mask_kernel(BlockMaskParams p) {
+  __shared__ uint32_t w[MAX_BLOCKS / 32];
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int qb = r % p.nb;
+  if (lane < MAX_BLOCKS / 32) w[lane] = lane == (qb >> 5) ? 1u << (qb & 31) : 0u;
+  __syncthreads();
+  const int e0 = min(max(p.ptr[r], 0), p.nnz);
+  const int e1 = min(max(p.ptr[r + 1], e0), p.nnz);
+  for (int e = e0 + lane; e < e1; e += 64) {
+    const int kb = p.idx[e];
+    if (kb >= 0 && kb < p.nb && (!p.causal || kb <= qb)) atomicOr(&w[kb >> 5], 1u << (kb & 31));
+  }
+  __syncthreads();
+  if (lane < p.W) p.mask[(size_t)r * p.W + lane] = w[lane];
+}
+
+void launch_block_mask(const BlockMaskParams& p, hipStream_t s) {
+  if (p.rows > 0) hipLaunchKernelGGL(block_mask_kernel, dim3((unsigned)p.rows), dim3(64), 0, s, p);
+}
+
 // d alpha_m = theta_hat_m * sum over slots of the position-weighted wedge
 // partials, summed in double in a fixed order (deterministic).
 __global__ void dalpha_kernel(DalphaParams p) {

@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256) void simt_fwd_kernel(SimtParams p) {
 #pragma unroll
       for (int c = 0; c < DL; ++c) s += qv[c] * ks[jj][c0 + c];
       s = group_sum(s) * p.scale;
-      const bool ok = row_ok && key < kend && (!p.causal || key <= i);
+      const bool ok = row_ok && key < kend && (!p.causal || key <= i) &&
+                      block_visible(p.bmask, p.nb, p.W, bh, i, key);
       if (ok) {
         const float mn = fmaxf(m, s);
         const float a = expf(m - mn);
@@ -181,7 +182,8 @@ __global__ __launch_bounds__(256) void simt_dq_kernel(SimtParams p) {
       }
       s = group_sum(s) * p.scale;
       dp = group_sum(dp);
-      const bool ok = row_ok && key < kend && (!p.causal || key <= i);
+      const bool ok = row_ok && key < kend && (!p.causal || key <= i) &&
+                      block_visible(p.bmask, p.nb, p.W, bh, i, key);
       const float pr = ok ? expf(s - lse) : 0.f;
       const float ds = pr * (dp - drow);
 #pragma unroll
@@ -255,7 +257,8 @@ __global__ __launch_bounds__(256) void simt_dkdv_kernel(SimtParams p) {
       }
       s = group_sum(s) * p.scale;
       dp = group_sum(dp);
-      const bool ok = key_ok && row < p.qend && (!p.causal || row >= key);
+      const bool ok = key_ok && row < p.qend && (!p.causal || row >= key) &&
+                      block_visible(p.bmask, p.nb, p.W, bh, row, key);
       const float pr = ok ? expf(s - lses[ii]) : 0.f;
       const float ds = pr * (dp - drs[ii]);
 #pragma unroll

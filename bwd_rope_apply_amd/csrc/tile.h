@@ -177,6 +177,83 @@ struct TileDMA {
   }
 };
 
+// Row offsets of the steps of a tile walk: dense (base + i STEP) or over a
+// block list in LDS (list[i / SPB] BLK + (i % SPB) STEP).  In block-list
+// mode the entry of step i + 2 is read from LDS during step i and made a
+// scalar after the step's closing wait, so no step stalls on an LDS read
+// before issuing its copies.
+template <int STEP, bool BL>
+struct Walk {
+  static constexpr int SPB = BLK / STEP;
+  const short* list;
+  int base, n;
+  int cur, next, raw;
+  __device__ __forceinline__ int at(int i) const {
+    if constexpr (BL) return __builtin_amdgcn_readfirstlane(list[i / SPB]) * BLK + (i % SPB) * STEP;
+    else return base + i * STEP;
+  }
+  __device__ __forceinline__ void init(const short* l, int b, int count) {
+    list = l; base = b; n = count; raw = 0;
+    cur = count > 0 ? at(0) : 0;
+    next = count > 1 ? at(1) : 0;
+  }
+  // during step i (i < n)
+  __device__ __forceinline__ void prefetch(int i) {
+    if constexpr (BL) raw = list[min(i + 2, n - 1) / SPB];
+  }
+  // after step i's closing wait
+  __device__ __forceinline__ void advance(int i) {
+    cur = next;
+    if constexpr (BL) next = __builtin_amdgcn_readfirstlane(raw) * BLK + ((i + 2) % SPB) * STEP;
+    else next = base + (i + 2) * STEP;
+  }
+};
+
+// Block lists for block-list attention.  One wave lists the set bits of a
+// visibility row [ceil(nb / 32) words] in ascending order, 64 candidate
+// blocks per ballot; the count is returned to every lane.
+__device__ __forceinline__ int row_blocks(const uint32_t* row, int nb, short* list, int lane) {
+  int n = 0;
+  for (int b0 = 0; b0 < nb; b0 += 64) {
+    const int b = b0 + lane;
+    const bool bit = b < nb && ((row[b >> 5] >> (b & 31)) & 1u);
+    const unsigned long long m = __ballot(bit);
+    const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (bit) list[n + before] = (short)b;
+    n += __popcll(m);
+  }
+  return n;
+}
+
+// Query blocks qb >= qb0 whose visibility row has bit kb, ascending, for a
+// workgroup of NT threads: each thread tests some rows, wave ballots land in
+// `col` (MAX_BLOCKS / 32 words of LDS), then wave 0 lists the set bits.
+// Every thread calls it; the count is returned to all.
+template <int NT>
+__device__ __forceinline__ int column_blocks(const uint32_t* bm, int nb, int W, int bh, int kb,
+                                             int qb0, uint32_t* col, short* list, int* count) {
+  for (int base = 0; base < nb; base += NT) {
+    const int qb = base + (int)threadIdx.x;
+    bool bit = false;
+    if (qb < nb && qb >= qb0)
+      bit = (bm[((size_t)bh * nb + qb) * W + (kb >> 5)] >> (kb & 31)) & 1u;
+    const unsigned long long b = __ballot(bit);
+    if ((threadIdx.x & 63) == 0 && base + (int)threadIdx.x < MAX_BLOCKS) {
+      const int w0 = (base + (int)threadIdx.x) >> 5;
+      col[w0] = (uint32_t)b;
+      if (w0 + 1 < MAX_BLOCKS / 32) col[w0 + 1] = (uint32_t)(b >> 32);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int c = row_blocks(col, nb, list, (int)threadIdx.x);
+    if (threadIdx.x == 0) *count = c;
+  }
+  __syncthreads();
+  return *count;
+}
+
 __device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0); }
 
 template <int D>

@@ -162,3 +162,38 @@ def get(name: str, B: Optional[int] = None, H: Optional[int] = None,
     if B is None and H is None and N is None and seed is None:
         return wl
     return wl.with_shape(B, H, N, seed)
+
+
+def block_lists(B: int, H: int, N: int, retrieved: int, causal: bool, seed: int,
+                noise: bool = False, block: int = 128):
+    """Seeded key-block lists for block-list attention: ``lists[b][h][qb]``
+    names, for each query block of ``block`` rows, ``retrieved`` key blocks
+    drawn uniformly without replacement from the other blocks it may see
+    (the earlier blocks under the causal mask, any other block otherwise) --
+    a stand-in for the retrieved (cluster, block) pairs of Multipole Semantic
+    Attention ("Retrieval-augmented approximation"), whose selection depends
+    on trained clusters.  The own block is implied and not listed.  With
+    ``noise`` each list also gets entries that must be ignored or merged:
+    duplicates, out-of-range indices and (causal) later blocks."""
+    nb = (N + block - 1) // block
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    out = []
+    for _ in range(B):
+        per_b = []
+        for _ in range(H):
+            per_h = []
+            for qb in range(nb):
+                cand = np.arange(qb) if causal else np.delete(np.arange(nb), qb)
+                k = min(retrieved, cand.size)
+                sel = [int(x) for x in rng.choice(cand, size=k, replace=False)] if k else []
+                if noise:
+                    if sel:
+                        sel.append(sel[0])
+                    sel += [-1, nb, nb + 7, qb]
+                    if causal and qb + 1 < nb:
+                        sel.append(qb + 1)
+                    rng.shuffle(sel)
+                per_h.append(sel)
+            per_b.append(per_h)
+        out.append(per_b)
+    return out

@@ -166,6 +166,28 @@ typedef struct {
   int unrotated_pairs;
   float scale;
   int pos_offset;
+  /* Block-list attention: exact attention in which each query block of 128
+   * rows sees its own (diagonal) key block plus the key blocks its list
+   * names, and no other key (Multipole Semantic Attention, "Retrieval-
+   * augmented approximation": the exact part, over retrieved block pairs and
+   * the local block diagonal).  Lists are CSR over the B*H*ceil(N/128)
+   * query blocks in [b][h][query block] order: the list of query block r is
+   * block_idx[block_ptr[r] .. block_ptr[r+1]-1], so block_ptr has
+   * B*H*ceil(N/128)+1 entries.  Both are DEVICE pointers to int32, read on
+   * the call's stream by the PREP stage, which turns them into a visibility
+   * bitmask in the workspace; the caller keeps them valid until then.
+   * block_ptr == NULL means dense attention (the default).  Entries of
+   * block_ptr are clamped to [0, block_nnz]; key blocks outside
+   * [0, ceil(N/128)), and under the causal mask blocks after the query's
+   * own, are ignored; duplicates are harmless.  O and LSE are over exactly
+   * the visible keys, so partial results over disjoint key sets merge
+   * through their LSEs.  Requires N <= 65536 (ERR_SHAPE otherwise),
+   * block_nnz >= 0 and block_idx non-NULL when block_nnz > 0 (ERR_ARG),
+   * 4-byte aligned pointers (ERR_ALIGN).  The bf16 path's cost scales with
+   * the listed blocks; the fp32 path tests every key. */
+  const int* block_ptr;
+  const int* block_idx;
+  int block_nnz;
 } rope_attn_options;
 
 /* The staged forward and backward with options (opts may be NULL).  A

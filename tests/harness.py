@@ -14,15 +14,27 @@ def to_device(x: np.ndarray, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
+def device_opts(opts, device="cuda"):
+    """The binding's options from the tests' dict: ``block_lists`` (nested
+    lists [b][h][query block] of key blocks) become CSR device tensors."""
+    if not opts or "block_lists" not in opts:
+        return opts
+    from bwd_rope_apply_amd import _lib
+    d = dict(opts)
+    d["blocks"] = _lib.block_csr(d.pop("block_lists"), device)
+    return d
+
+
 def run_gpu(inp: W.Inputs, causal=None, alpha=True, want_dalpha=True, opts=None):
     """Forward and backward on the GPU; returns float64 numpy arrays.  opts:
-    a dict of frequency-schedule options (unrotated_pairs, scale, pos_offset)."""
+    a dict of options (unrotated_pairs, scale, pos_offset, block_lists)."""
     import torch
     from bwd_rope_apply_amd import fwd, bwd
     wl = inp.wl
     causal = wl.causal if causal is None else causal
     q, k, v, do = (to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
     a = to_device(inp.alpha) if alpha else None
+    opts = device_opts(opts)
     o, lse = fwd(q, k, v, wl.base, a, causal, opts=opts)
     dq, dk, dv, da = bwd(q, k, v, o, do, lse, wl.base, a, causal, want_dalpha=want_dalpha, opts=opts)
     torch.cuda.synchronize()
@@ -38,6 +50,8 @@ def oracle_kwargs(D: int, opts=None) -> dict:
         kw["rot"] = D // 2 - opts["unrotated_pairs"]
     if opts.get("scale"):
         kw["scale"] = float(np.float32(opts["scale"]))
+    if opts.get("block_lists") is not None:
+        kw["blocks"] = opts["block_lists"]
     return kw
 
 

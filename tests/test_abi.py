@@ -97,3 +97,33 @@ def test_status_strings(lib):
     for s in range(-7, 1):
         assert lib.rope_attn_status_string(s)
     assert lib.rope_attn_status_string(-99) == b"unknown status"
+
+
+@pytest.mark.parametrize("N,ptr,idx,nnz,status", [
+    (65537, A, A, 4, -2),      # more than 512 blocks per head
+    (256, A, A, -1, -7),       # negative entry count
+    (256, A, None, 3, -7),     # entries without an index array
+    (256, A + 2, A, 4, -4),    # misaligned offsets
+    (256, A, A + 1, 4, -4),    # misaligned indices
+])
+def test_block_list_validation(lib, N, ptr, idx, nnz, status):
+    """Invalid block lists are rejected before any launch (D = 64)."""
+    import ctypes
+    from bwd_rope_apply_amd import _lib
+    op = _lib.Options(0, 0.0, 0, ptr, idx, nnz)
+    args = (A, A, A, A, A, 1, 1, N, 64, 1, 1e4, None, 1, A, 1 << 40, None)
+    assert lib.rope_attn_fwd_ex(63, ctypes.addressof(op), *args) == status
+    bargs = [A] * 10 + [1, 1, N, 64, 1, 1e4, None, 1, A, 1 << 40, None]
+    assert lib.rope_attn_bwd_ex(63, ctypes.addressof(op), *bargs) == status
+
+
+def test_workspace_covers_block_lists(lib):
+    """The workspace queries take no options, so their size must hold the
+    block-list layout too (visibility mask, and the dQ/dK/dV slots for the
+    one-block exact corner) at lengths where the dense corner is larger."""
+    for N in (256, 8192, 20000, 65536):
+        f = lib.rope_attn_fwd_workspace_bytes(1, 4, N, 128, 1, 1)
+        b = lib.rope_attn_bwd_workspace_bytes(1, 4, N, 128, 1, 1)
+        nb = (N + 127) // 128
+        assert f >= 4 * 4 * nb * ((nb + 31) // 32)
+        assert b > f
