@@ -197,3 +197,100 @@ def block_lists(B: int, H: int, N: int, retrieved: int, causal: bool, seed: int,
             per_b.append(per_h)
         out.append(per_b)
     return out
+
+
+# ---------------------------------------------------------------- token sets
+# Inputs of Gram-threshold token selection ("Cascade token selection for
+# transformer attention acceleration"): one layer's token activations
+# [B, T, d] and a stack of layers for the cascade.  The pages measure
+# T = 512 with the hidden sizes of GPT-2 (768) and GPT-J / OPT (4096) at
+# tau = 0.30, and project to T = 8192 (Experimental results).  Trained
+# activations are not available, so tokens are drawn around random
+# directions ("topics") with mixed spreads: tight groups make near-duplicates
+# (cosine ~0.95-0.99, redundant at tau = 0.30), loose groups do not (~0.6-0.8),
+# with per-token gains; deeper layers add a small residual perturbation, the
+# depth coherence the cascade relies on (Methodology).
+
+
+@dataclasses.dataclass(frozen=True)
+class TokenWorkload:
+    name: str
+    B: int
+    T: int
+    d: int
+    dtype: str            # "bf16" or "fp16" storage
+    tau: float
+    group: int            # mean tokens per direction
+    spreads: Tuple[float, ...]   # squared noise-to-signal ratio per direction, drawn from these
+    drift: float          # squared relative size of the per-layer residual perturbation
+    seed: int
+    note: str = ""
+
+    def with_shape(self, B=None, T=None, d=None, seed=None) -> "TokenWorkload":
+        return dataclasses.replace(
+            self, B=B or self.B, T=T or self.T, d=d or self.d,
+            seed=self.seed if seed is None else seed,
+            name=f"{self.name}[B{B or self.B},T{T or self.T},d{d or self.d}]")
+
+
+_SPREADS = (0.01, 0.03, 0.08, 0.12, 0.3)
+
+TOKEN_WORKLOADS: Dict[str, TokenWorkload] = {
+    "gram_gpt2_512": TokenWorkload("gram_gpt2_512", 1, 512, 768, "bf16", 0.30, 16, _SPREADS, 0.02,
+                                   seed=2001, note="T = 512, GPT-2 hidden size"),
+    "gram_gptj_512": TokenWorkload("gram_gptj_512", 1, 512, 4096, "bf16", 0.30, 16, _SPREADS, 0.02,
+                                   seed=2002, note="T = 512, GPT-J / OPT hidden size"),
+    "gram_8k": TokenWorkload("gram_8k", 1, 8192, 4096, "bf16", 0.30, 16, _SPREADS, 0.02,
+                             seed=2003, note="the projected long sequence, T = 8192, d = 4096"),
+}
+
+GRAM_HEADLINE = "gram_8k"
+
+
+def get_tokens(name: str, B=None, T=None, d=None, seed=None) -> TokenWorkload:
+    wl = TOKEN_WORKLOADS[name]
+    if B is None and T is None and d is None and seed is None:
+        return wl
+    return wl.with_shape(B, T, d, seed)
+
+
+def _to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x.astype(np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    if dtype == "fp16":
+        return x32.astype(np.float16)
+    return x32
+
+
+def storage_to_f64(x: np.ndarray) -> np.ndarray:
+    """Exact upcast of stored token bits (bf16 as uint16, fp16, fp32)."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return x.astype(np.float64)
+
+
+def make_tokens(wl: TokenWorkload, layers: int = 1):
+    """Stored tokens of ``layers`` consecutive layers: a list of [B, T, d]
+    arrays (bf16 bits as uint16, or fp16).  Streams: one PCG64 per layer,
+    spawned from SeedSequence(seed); layer 0 draws the directions, spreads,
+    assignments, gains and noise in that order; layer l > 0 adds
+    N(0, drift * gain^2 / d) per entry to layer l - 1 (before rounding)."""
+    streams = np.random.SeedSequence(wl.seed).spawn(max(1, layers))
+    rng = np.random.Generator(np.random.PCG64(streams[0]))
+    n_dir = max(1, wl.T // wl.group)
+    shape = (wl.B, wl.T, wl.d)
+    dirs = rng.normal(size=(wl.B, n_dir, wl.d))
+    dirs /= np.linalg.norm(dirs, axis=-1, keepdims=True)
+    spread = rng.choice(np.asarray(wl.spreads), size=(wl.B, n_dir))
+    z = rng.integers(0, n_dir, size=(wl.B, wl.T))
+    gain = rng.uniform(0.5, 3.0, size=(wl.B, wl.T, 1))
+    b = np.arange(wl.B)[:, None]
+    x = dirs[b, z] + rng.normal(size=shape) * np.sqrt(spread[b, z] / wl.d)[..., None]
+    x = x * gain
+    out = [_to_storage(x, wl.dtype)]
+    for l in range(1, layers):
+        r = np.random.Generator(np.random.PCG64(streams[l]))
+        x = x + r.normal(size=shape) * (gain * np.sqrt(wl.drift / wl.d))
+        out.append(_to_storage(x, wl.dtype))
+    return out
