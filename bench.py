@@ -17,6 +17,8 @@ backward.  One workspace serves both passes: the backward reuses the
 forward's rotated fp16 planes and frequency table (saved activations) and
 prepares only dO and D.
 
+--gram times Gram-threshold token selection instead (see bench_gram).
+
 --retrieved K times block-list attention instead (each 128-row query block
 sees its own block and K seeded key blocks, the exact part of Multipole
 Semantic Attention); flops then count the visible pairs only.
@@ -61,6 +63,9 @@ def parse():
     ap.add_argument("--retrieved", type=int, default=-1,
                     help="block-list attention: key blocks retrieved per 128-row query block "
                          "(seeded, uniform among the blocks it may see); -1 = dense")
+    ap.add_argument("--gram", action="store_true",
+                    help="time Gram-threshold token selection (and one cascade step) instead")
+    ap.add_argument("--gram-workload", default="gram_8k")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_8k.json"),
                     help="JSON with measured HBM bytes per launch of the MFMA kernels (used only "
                          "if it was taken on the current kernel source)")
@@ -135,6 +140,116 @@ def visible_pairs(lists, N: int, causal: bool) -> int:
     return total
 
 
+def gram_cpu_baseline(x, tau, d):
+    """The float64 oracle's selection on the first tokens of the sequence (a
+    bounded sample of the same workload), timed on the host cores."""
+    import numpy as np
+    from oracle import gram
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    Ts = min(x.shape[0], 2048)
+    xs = np.ascontiguousarray(x[:Ts])
+    t0 = time.perf_counter()
+    gram.select(xs, tau)
+    dt = time.perf_counter() - t0
+    return {"value": d * Ts * (Ts - 1) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"first {Ts} of {x.shape[0]} tokens (d={d}), float64 "
+                                        f"selection, {dt:.2f} s"}
+
+
+def bench_gram(args):
+    """Gram-threshold selection ("Cascade token selection for transformer
+    attention acceleration"): one step = the full selection of one layer's
+    tokens (causal T x T Gram product, d T (T - 1) flops); one cascade step
+    on the next layer, inheriting that selection, is timed beside it."""
+    import numpy as np
+    import torch
+    from bwd_rope_apply_amd import workloads as W
+    from bwd_rope_apply_amd import _lib
+
+    wl = W.get_tokens(args.gram_workload)
+    x0s, x1s = (a[0] for a in W.make_tokens(wl, layers=2))
+    dev = torch.device("cuda:0")
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x0, x1 = dev_t(x0s), dev_t(x1s)
+    T, d = wl.T, wl.d
+    lib = _lib.load()
+    ws = torch.empty(int(lib.gram_select_workspace_bytes(1, T, d)), dtype=torch.uint8, device=dev)
+    wsc = torch.empty(int(lib.gram_cascade_workspace_bytes(T, d)), dtype=torch.uint8, device=dev)
+    m = torch.empty((1, T), dtype=torch.float32, device=dev)
+    rep = torch.empty((1, T), dtype=torch.uint8, device=dev)
+    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    mc, repc = torch.empty((T,), dtype=torch.float32, device=dev), torch.empty((T,), dtype=torch.uint8, device=dev)
+    cntc = torch.empty((1,), dtype=torch.int32, device=dev)
+    stages = [("prep", _lib.GRAM_STAGE_PREP), ("gram", _lib.GRAM_STAGE_GRAM), ("decide", _lib.GRAM_STAGE_DECIDE)]
+    prev = rep[0]
+
+    def step(ev=None):
+        for i, (_, bit) in enumerate(stages):
+            if ev is not None:
+                ev[i].record()
+            _lib.gram_select(x0, wl.tau, workspace=ws, out=(m, rep, cnt), stages=bit)
+        if ev is not None:
+            ev[3].record()
+        _lib.gram_cascade(x1, wl.tau, prev, workspace=wsc, out=(mc, repc, cntc))
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    gram_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    casc = np.array([e[3].elapsed_time(e[4]) for e in evs])
+    flops = float(d) * T * (T - 1)
+    ms = float(np.median(sel))
+    r_prev, r_new = int(rep.sum().item()), int(repc.sum().item())
+    kept = int((repc.bool() & rep[0].bool()).sum().item())
+    line = {
+        "metric": f"Gram-threshold selection TFLOP/s (causal T x T Gram of normalised tokens), T={T} d={d}",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": 1, "T": T, "d": d, "tau": wl.tau, "storage": wl.dtype,
+                   "flops_per_step": flops, "wall_ms_per_step_incl_cascade": round(wall * 1e3 / args.steps, 4)},
+        "roofline": {"bound": "mfma", "kernel": "gram_max_kernel", "achieved": round(flops / (gram_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (gram_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_ms": round(gram_ms, 4)},
+        "stages_ms": {n: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])), 4)
+                      for i, (n, _) in enumerate(stages)},
+        "cascade": {"ms_median": round(float(np.median(casc)), 4), "inherited": r_prev, "kept": kept,
+                    "added": r_new - kept, "selected": r_new,
+                    "gram_ops_vs_full": round((r_prev * r_prev + (T - r_prev) * r_prev) / float(T * T), 4),
+                    "speedup_vs_full_selection": round(ms / float(np.median(casc)), 3)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = gram_cpu_baseline(W.storage_to_f64(x0s), wl.tau, d)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,6 +257,9 @@ def main():
               "(heads are independent, a multi-GPU run would shard them and all-reduce dalpha)",
               file=sys.stderr)
         sys.exit(2)
+    if args.gram:
+        bench_gram(args)
+        return
 
     import numpy as np
     import torch

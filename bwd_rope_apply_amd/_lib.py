@@ -103,6 +103,17 @@ def load() -> ctypes.CDLL:
     lib.rope_attn_bwd_ex.restype = i
     lib.rope_attn_status_string.argtypes = [i]
     lib.rope_attn_status_string.restype = ctypes.c_char_p
+    f = ctypes.c_float
+    lib.gram_select_workspace_bytes.argtypes = [i, i, i]
+    lib.gram_select_workspace_bytes.restype = sz
+    lib.gram_cascade_workspace_bytes.argtypes = [i, i]
+    lib.gram_cascade_workspace_bytes.restype = sz
+    lib.gram_select.argtypes = [vp, i, i, i, i, f, vp, vp, vp, vp, sz, vp]
+    lib.gram_select.restype = i
+    lib.gram_select_stages.argtypes = [ctypes.c_uint] + lib.gram_select.argtypes
+    lib.gram_select_stages.restype = i
+    lib.gram_cascade.argtypes = [vp, i, i, i, f, vp, vp, vp, vp, vp, sz, vp]
+    lib.gram_cascade.restype = i
     _lib = lib
     return lib
 
@@ -218,3 +229,73 @@ def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, works
                               _ptr(workspace), workspace.numel(), _stream(q.device))
     _check("rope_attn_bwd", st)
     return dq, dk, dv, da
+
+
+# ------------------------------------------------------------ token selection
+GRAM_BF16, GRAM_FP16 = 1, 2
+GRAM_STAGE_PREP, GRAM_STAGE_GRAM, GRAM_STAGE_DECIDE, GRAM_STAGE_ALL = 1, 2, 4, 7
+
+
+def _gram_dtype(x) -> int:
+    import torch
+    if x.dtype == torch.bfloat16:
+        return GRAM_BF16
+    if x.dtype == torch.float16:
+        return GRAM_FP16
+    raise TypeError(f"tokens must be bfloat16 or float16, got {x.dtype}")
+
+
+def gram_select(x, tau: float, workspace=None, out=None, stages: int = GRAM_STAGE_ALL):
+    """Gram-threshold selection of each sequence of ``x`` ([B, T, d] or
+    [T, d], bf16 or fp16, on the device).  Returns (max_cos float32, rep
+    uint8, count int32 [B]) with the leading shape of ``x``.  ``stages``
+    selects stage bits (default: all)."""
+    import torch
+    lib = load()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() not in (2, 3):
+        raise ValueError("x must be a contiguous [B, T, d] or [T, d] device tensor")
+    xb = x if x.dim() == 3 else x.unsqueeze(0)
+    B, T, d = (int(v) for v in xb.shape)
+    dt = _gram_dtype(x)
+    if out is None:
+        m = torch.empty((B, T), dtype=torch.float32, device=x.device)
+        rep = torch.empty((B, T), dtype=torch.uint8, device=x.device)
+        cnt = torch.empty((B,), dtype=torch.int32, device=x.device)
+    else:
+        m, rep, cnt = out
+    nbytes = int(lib.gram_select_workspace_bytes(B, T, d))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.gram_select_stages(stages, _ptr(xb), B, T, d, dt, float(tau), _ptr(m), _ptr(rep),
+                                _ptr(cnt), _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check("gram_select", st)
+    if x.dim() == 2:
+        return m[0], rep[0], cnt
+    return m, rep, cnt
+
+
+def gram_cascade(x, tau: float, prev, workspace=None, out=None):
+    """One cascade step on one sequence ``x`` [T, d] (bf16 or fp16, on the
+    device) with the inherited set ``prev`` ([T] uint8 flags on the device).
+    Returns (max_cos float32 [T], rep uint8 [T], count int32 [1])."""
+    import torch
+    lib = load()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous [T, d] device tensor")
+    T, d = (int(v) for v in x.shape)
+    if prev.shape != (T,) or prev.dtype != torch.uint8 or not prev.is_contiguous() or not prev.is_cuda:
+        raise ValueError("prev must be a contiguous uint8 [T] device tensor")
+    dt = _gram_dtype(x)
+    if out is None:
+        m = torch.empty((T,), dtype=torch.float32, device=x.device)
+        rep = torch.empty((T,), dtype=torch.uint8, device=x.device)
+        cnt = torch.empty((1,), dtype=torch.int32, device=x.device)
+    else:
+        m, rep, cnt = out
+    nbytes = int(lib.gram_cascade_workspace_bytes(T, d))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.gram_cascade(_ptr(x), T, d, dt, float(tau), _ptr(prev), _ptr(m), _ptr(rep), _ptr(cnt),
+                          _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check("gram_cascade", st)
+    return m, rep, cnt

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librope_attn.so")
-SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "corner.hip"]
+SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "corner.hip", "gram.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,13 +8,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rope_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rope_attn.h", "gram_select.h")]
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rope_attn_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:rope_attn|gram)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +28,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["rope_attn_bwd", "rope_attn_bwd_ex", "rope_attn_bwd_stages",
+    assert _declared() == ["gram_cascade", "gram_cascade_workspace_bytes", "gram_select",
+                           "gram_select_stages", "gram_select_workspace_bytes",
+                           "rope_attn_bwd", "rope_attn_bwd_ex", "rope_attn_bwd_stages",
                            "rope_attn_bwd_workspace_bytes", "rope_attn_fwd", "rope_attn_fwd_ex",
                            "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
                            "rope_attn_status_string"]
@@ -127,3 +131,42 @@ def test_workspace_covers_block_lists(lib):
         nb = (N + 127) // 128
         assert f >= 4 * 4 * nb * ((nb + 31) // 32)
         assert b > f
+
+
+def test_gram_workspace_queries(lib):
+    assert lib.gram_select_workspace_bytes(1, 8192, 4096) >= 8 * 8192
+    assert lib.gram_cascade_workspace_bytes(8192, 4096) >= 17 * 8192
+    assert lib.gram_select_workspace_bytes(1, 512, 100) == 0        # d not a multiple of 64
+    assert lib.gram_select_workspace_bytes(0, 512, 768) == 0
+    assert lib.gram_select_workspace_bytes(1, 1 << 21, 64) == 0     # T > 2^20
+    assert lib.gram_cascade_workspace_bytes(1 << 16, 1 << 16) == 0  # T d > 2^31
+
+
+W_ = 1 << 30
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1, 64, 64, 1, 0.3, A, A, None, A, W_, None), -1),      # x
+    ((A, 1, 64, 64, 1, 0.3, None, A, None, A, W_, None), -1),      # max_cos
+    ((A, 1, 64, 64, 3, 0.3, A, A, None, A, W_, None), -3),         # dtype
+    ((A, 1, 64, 96, 1, 0.3, A, A, None, A, W_, None), -2),         # d
+    ((A, 1, 0, 64, 1, 0.3, A, A, None, A, W_, None), -2),          # T
+    ((A, 1, 64, 64, 1, -0.1, A, A, None, A, W_, None), -7),        # tau < 0
+    ((A, 1, 64, 64, 1, float("nan"), A, A, None, A, W_, None), -7),
+    ((A + 8, 1, 64, 64, 1, 0.3, A, A, None, A, W_, None), -4),     # x alignment
+    ((A, 1, 64, 64, 1, 0.3, A + 2, A, None, A, W_, None), -4),     # max_cos alignment
+    ((A, 1, 64, 64, 1, 0.3, A, A, None, A + 16, W_, None), -4),    # workspace alignment
+    ((A, 1, 64, 64, 1, 0.3, A, A, None, A, 16, None), -5),         # workspace size
+])
+def test_gram_select_validation(lib, args, status):
+    assert lib.gram_select(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 64, 64, 1, 0.3, None, A, A, None, A, W_, None), -1),      # prev
+    ((A, 64, 64, 2, float("inf"), A, A, A, None, A, W_, None), -7),
+    ((A, 64, 128, 0, 0.3, A, A, A, None, A, W_, None), -3),
+    ((A, 64, 64, 1, 0.3, A, A, A, None, A, 64, None), -5),
+])
+def test_gram_cascade_validation(lib, args, status):
+    assert lib.gram_cascade(*args) == status
