@@ -8,6 +8,8 @@
 // float32 accumulator), and the inverse norms (float32 sums of exact
 // squares) scale the result in the epilogue.
 #include <limits.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -47,6 +49,7 @@ struct Tiles {
 typedef Tiles<128, 128, 2, 2> SmallTiles;
 typedef Tiles<256, 256, 4, 2> LargeTiles;
 
+constexpr int MAX_SPLITS = 16;     // feature-axis splits of a tile, at most
 constexpr int ENC_NEG_INF = (int)(0xff800000u ^ 0x7fffffffu);
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -70,6 +73,8 @@ struct GramParams {
   int B, T, d;
   int tri;                      // queries and keys are one list: lower-triangle tiles
   int tiles;                    // tiles per sequence in the grid (an upper bound)
+  int splits;                   // feature-axis splits per tile (1: unsplit)
+  float* part;                  // split partial products (splits > 1)
   int contiguous;               // hand each XCD a contiguous run of tiles (every id is real work)
 };
 
@@ -90,19 +95,117 @@ struct Frag<false> {
   }
 };
 
-// Workgroup = a 128-key x 128-query tile (4 waves, 64 x 64 each, keys along
-// the MFMA's m so a lane holds one query's column).  The feature axis is
-// streamed in 64-wide stages through double-buffered LDS by direct
-// global->LDS copies; each tile row carries a 16-byte pad, so the 32 rows a
-// 128-bit fragment read touches fall on distinct banks.  The epilogue
-// scales by the key norms, masks keys at or after the query (and keys not
-// in the list or not valid), reduces each query's column to its maximum and
-// merges it into the global maximum with an integer atomic max (exact and
-// order-independent).
-template <bool BF16, class C>
+// Tile decode shared by the Gram kernel and the split reduction: work id ->
+// (sequence, tile slot b * tiles + tile, query and key tile, split, with
+// `splits` ids per tile); false when the id is past the real work or the
+// tile holds no key before any of its queries.
+template <class C>
+__device__ __forceinline__ bool decode_tile(const GramParams& p, int id, int splits, int& b, int& slot,
+                                            int& q0, int& k0, int& split, int& nq, int& nk) {
+  const int per_seq = p.tiles * splits;
+  b = id / per_seq;
+  const int within = id - b * per_seq;
+  const int tid = within / splits;
+  split = within - tid * splits;
+  slot = b * p.tiles + tid;
+  nq = p.qn ? *p.qn : p.T;
+  nk = p.kn ? *p.kn : p.T;
+  int qt, kt;
+  if (p.tri) {
+    // the largest qt with tri_before(qt) <= tid
+    int lo = 0, hi = (p.T + C::QT - 1) / C::QT;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (C::tri_before(mid) <= tid) lo = mid;
+      else hi = mid;
+    }
+    qt = lo;
+    kt = tid - (int)C::tri_before(qt);
+    if (qt * C::QT >= nq) return false;
+  } else {
+    const int ntk = (nk + C::KT - 1) / C::KT, ntq = (nq + C::QT - 1) / C::QT;
+    if (tid >= ntk * ntq) return false;
+    qt = tid / ntk;
+    kt = tid - qt * ntk;
+  }
+  q0 = qt * C::QT;
+  k0 = kt * C::KT;
+  const int qlast = min(q0 + C::QT, nq) - 1;
+  const int tq = p.qidx ? p.qidx[qlast] : qlast;
+  const int tk = p.kidx ? p.kidx[k0] : k0;
+  return tk < tq;
+}
+
+// token, inverse norm and mask of the tile's keys and queries, into LDS
+// (keys not in the list or not valid get INT_MAX, which no query exceeds)
+template <class C>
+__device__ __forceinline__ void tile_rows(const GramParams& p, size_t seq, int q0, int k0, int nq,
+                                          int nk, int* kpos, int* qpos, float* kinv, float* qinv) {
+  for (int t = threadIdx.x; t < C::KT + C::QT; t += C::NT) {
+    if (t < C::KT) {
+      const int i = k0 + t;
+      int tok = INT_MAX;
+      float iv = 0.f;
+      if (i < nk) {
+        const int tk = p.kidx ? p.kidx[i] : i;
+        iv = p.inv[seq + tk];
+        tok = (p.kvalid && !p.kvalid[tk]) ? INT_MAX : tk;
+      }
+      kpos[t] = tok;
+      kinv[t] = iv;
+    } else {
+      const int r = t - C::KT, i = q0 + r;
+      int tok = -1;
+      float iv = 0.f;
+      if (i < nq) {
+        tok = p.qidx ? p.qidx[i] : i;
+        iv = p.inv[seq + tok];
+      }
+      qpos[r] = tok;
+      qinv[r] = iv;
+    }
+  }
+}
+
+// Each query's column of the products scaled to cosines, masked to keys
+// before the query, reduced to its maximum and merged into the global
+// maximum with an integer atomic max (exact and order-independent).
+template <class C>
+__device__ __forceinline__ void tile_max(const f32x16 (&acc)[C::MB][C::NB], const GramParams& p,
+                                         size_t seq, const int* kpos, const int* qpos,
+                                         const float* kinv, const float* qinv, int w) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int kh = w / C::WQ, qh = w % C::WQ;
+#pragma unroll
+  for (int n = 0; n < C::NB; ++n) {
+    const int ql_ = qh * (C::QT / C::WQ) + n * 32 + l32;
+    const int qtok = qpos[ql_];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl_ = kh * (C::KT / C::WK) + m * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float v = acc[m][n][r] * kinv[kl_];
+        if (kpos[kl_] < qtok) mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (g == 0 && qtok >= 0 && mx > -INFINITY) atomicMax(p.mkey + seq + qtok, enc(mx * qinv[ql_]));
+  }
+}
+
+// Workgroup = a KT-key x QT-query tile (keys along the MFMA's m, so a lane
+// holds one query's column).  The feature axis is streamed in 64-wide
+// stages through double-buffered LDS by direct global->LDS copies; each
+// tile row carries a 16-byte pad, so the 32 rows a 128-bit fragment read
+// touches fall on distinct banks.  With SPLIT the workgroup covers one of
+// p.splits contiguous ranges of the stages and stores its partial products
+// (in the accumulators' own lane layout) for gram_reduce_kernel; otherwise
+// it finishes the tile itself.
+template <bool BF16, class C, bool SPLIT>
 __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gram_max_kernel(GramParams p) {
   typedef typename Frag<BF16>::T vec;
-  constexpr int KT = C::KT, QT = C::QT, WK = C::WK, WQ = C::WQ, NW = C::NW, NT = C::NT;
+  constexpr int KT = C::KT, QT = C::QT, WK = C::WK, WQ = C::WQ, NW = C::NW;
   constexpr int KBYTES = C::KBYTES, STAGE = C::STAGE, NBK = C::NBK, NBQ = C::NBQ;
   constexpr int PWK = C::PWK, PWQ = C::PWQ, MB = C::MB, NB = C::NB;
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];  // [stage][keys | queries]
@@ -121,60 +224,10 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gram_max_kernel(GramParam
     const int per = nblk >> 3, rem = nblk & 7;
     id = xcd < rem ? xcd * (per + 1) + jx : rem * (per + 1) + (xcd - rem) * per + jx;
   }
-  const int b = id / p.tiles, tid = id % p.tiles;
-  const int nq = p.qn ? *p.qn : p.T, nk = p.kn ? *p.kn : p.T;
-  int qt, kt;
-  if (p.tri) {
-    // the largest qt with tri_before(qt) <= tid
-    int lo = 0, hi = (p.T + QT - 1) / QT;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (C::tri_before(mid) <= tid) lo = mid;
-      else hi = mid;
-    }
-    qt = lo;
-    kt = tid - (int)C::tri_before(qt);
-    if (qt * QT >= nq) return;
-  } else {
-    const int ntk = (nk + KT - 1) / KT, ntq = (nq + QT - 1) / QT;
-    if (tid >= ntk * ntq) return;
-    qt = tid / ntk;
-    kt = tid - qt * ntk;
-  }
-  const int q0 = qt * QT, k0 = kt * KT;
-  // no key of the tile precedes the tile's last query: nothing to do
-  {
-    const int qlast = min(q0 + QT, nq) - 1;
-    const int tq = p.qidx ? p.qidx[qlast] : qlast;
-    const int tk = p.kidx ? p.kidx[k0] : k0;
-    if (tk >= tq) return;
-  }
+  int b, slot, q0, k0, split, nq, nk;
+  if (!decode_tile<C>(p, id, SPLIT ? p.splits : 1, b, slot, q0, k0, split, nq, nk)) return;
   const size_t seq = (size_t)b * p.T;
-
-  for (int t = threadIdx.x; t < KT + QT; t += NT) {
-    if (t < KT) {
-      const int i = k0 + t;
-      int tok = INT_MAX;
-      float iv = 0.f;
-      if (i < nk) {
-        const int tk = p.kidx ? p.kidx[i] : i;
-        iv = p.inv[seq + tk];
-        tok = (p.kvalid && !p.kvalid[tk]) ? INT_MAX : tk;
-      }
-      kpos[t] = tok;
-      kinv[t] = iv;
-    } else {
-      const int r = t - KT, i = q0 + r;
-      int tok = -1;
-      float iv = 0.f;
-      if (i < nq) {
-        tok = p.qidx ? p.qidx[i] : i;
-        iv = p.inv[seq + tok];
-      }
-      qpos[r] = tok;
-      qinv[r] = iv;
-    }
-  }
+  if (!SPLIT) tile_rows<C>(p, seq, q0, k0, nq, nk, kpos, qpos, kinv, qinv);
 
   // per-lane copy offsets (bytes from the start of the sequence's first
   // feature stage): copy block w + NW i of an operand tile, 16 bytes a lane;
@@ -212,12 +265,13 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gram_max_kernel(GramParam
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[a][c] = f32x16{};
   const int nc = p.d / KC;
-  issue(0, 0);
+  const int c0 = SPLIT ? split * nc / p.splits : 0, c1 = SPLIT ? (split + 1) * nc / p.splits : nc;
+  issue(c0, 0);
   wait_lds_copies();
   __syncthreads();
-  for (int c = 0; c < nc; ++c) {
-    const int cur = c & 1;
-    if (c + 1 < nc) issue(c + 1, cur ^ 1);
+  for (int c = c0; c < c1; ++c) {
+    const int cur = (c - c0) & 1;
+    if (c + 1 < c1) issue(c + 1, cur ^ 1);
     __builtin_amdgcn_sched_barrier(0);  // keep the next stage's copies ahead of the products
     const char* kl = lds + cur * STAGE + (kh * (KT / WK) + l32) * RSB + 16 * g;
     const char* ql = lds + cur * STAGE + KBYTES + (qh * (QT / WQ) + l32) * RSB + 16 * g;
@@ -237,29 +291,91 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gram_max_kernel(GramParam
     __syncthreads();
   }
 
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const int ql_ = qh * (QT / WQ) + n * 32 + l32;
-    const int qtok = qpos[ql_];
-    float mx = -INFINITY;
+  if (SPLIT) {
+    // partial products of this split, [tile slot][wave][split][block][reg/4][lane][4]
+    float4* dst = reinterpret_cast<float4*>(p.part) +
+                  (((size_t)slot * NW + w) * p.splits + split) * (size_t)(MB * NB * 4 * 64) + lane;
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl_ = kh * (KT / WK) + m * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float v = acc[m][n][r] * kinv[kl_];
-        if (kpos[kl_] < qtok) mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (g == 0 && qtok >= 0 && mx > -INFINITY) atomicMax(p.mkey + seq + qtok, enc(mx * qinv[ql_]));
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dst[((m * NB + n) * 4 + r) * 64] =
+              make_float4(acc[m][n][4 * r], acc[m][n][4 * r + 1], acc[m][n][4 * r + 2], acc[m][n][4 * r + 3]);
+    return;
   }
+  tile_max<C>(acc, p, seq, kpos, qpos, kinv, qinv, w);
+}
+
+// Sum of a split tile's partial products in split order (deterministic),
+// then the unsplit epilogue, element-wise: one thread per 4 accumulator
+// registers (4 consecutive keys of one query) of one tile slot, so the
+// partial reads of every split are in flight at once and spread over the
+// chip; each thread merges its 4 keys' maximum into its query's.
+template <class C>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(GramParams p, int slots) {
+  constexpr int MB = C::MB, NB = C::NB, NW = C::NW;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int lane = (int)(gid & 63);
+  long long rest = gid >> 6;
+  const int r4 = (int)(rest % 4);
+  rest /= 4;
+  const int n = (int)(rest % NB);
+  rest /= NB;
+  const int m = (int)(rest % MB);
+  rest /= MB;
+  const int w = (int)(rest % NW);
+  const long long sl = rest / NW;
+  if (sl >= slots) return;
+  int b, slot, q0, k0, split, nq, nk;
+  if (!decode_tile<C>(p, (int)sl, 1, b, slot, q0, k0, split, nq, nk)) return;
+  const size_t seq = (size_t)b * p.T;
+  const float4* src = reinterpret_cast<const float4*>(p.part) +
+                      ((size_t)slot * NW + w) * p.splits * (size_t)(MB * NB * 4 * 64) +
+                      ((m * NB + n) * 4 + r4) * 64 + lane;
+  float4 u[MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s)  // all loads first, then the sum in split order
+    if (s < p.splits) u[s] = src[(size_t)s * (MB * NB * 4 * 64)];
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s)
+    if (s < p.splits) {
+      v.x += u[s].x;
+      v.y += u[s].y;
+      v.z += u[s].z;
+      v.w += u[s].w;
+    }
+  const int l32 = lane & 31, g = lane >> 5, kh = w / C::WQ, qh = w % C::WQ;
+  const int qi = q0 + qh * (C::QT / C::WQ) + n * 32 + l32;
+  if (qi >= nq) return;
+  const int qtok = p.qidx ? p.qidx[qi] : qi;
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ki = k0 + kh * (C::KT / C::WK) + m * 32 + 8 * r4 + 4 * g + j;
+    if (ki < nk) {
+      const int tk = p.kidx ? p.kidx[ki] : ki;
+      if (tk < qtok && !(p.kvalid && !p.kvalid[tk])) mx = fmaxf(mx, vv[j] * p.inv[seq + tk]);
+    }
+  }
+  if (mx > -INFINITY) atomicMax(p.mkey + seq + qtok, enc(mx * p.inv[seq + qtok]));
 }
 
 // inverse norms, one wave per token: float32 sum of exact squares
 template <bool BF16>
-__global__ __launch_bounds__(256) void gram_norm_kernel(const void* x, float* inv, int rows, int d) {
+// (with mkey set: also resets the row's running maximum, and the first row
+// of each sequence of T resets that sequence's count)
+__global__ __launch_bounds__(256) void gram_norm_kernel(const void* x, float* inv, int rows, int d,
+                                                        int* mkey, int* count, int T) {
   const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  if (mkey && lane == 0) {
+    mkey[row] = ENC_NEG_INF;
+    if (count && row % T == 0) count[row / T] = 0;
+  }
   const uint4* xr = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + (size_t)row * d * 2);
   float s = 0.f;
   for (int c = lane; c < d / 8; c += 64) {
@@ -282,12 +398,6 @@ __global__ __launch_bounds__(256) void gram_norm_kernel(const void* x, float* in
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
   if (lane == 0) inv[row] = s > 0.f ? 1.0f / sqrtf(s) : 0.f;
-}
-
-__global__ void gram_fill_kernel(int* mkey, int n, int* count, int B) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) mkey[i] = ENC_NEG_INF;
-  if (count && i < B) count[i] = 0;
 }
 
 // decisions of the selection rule; blockIdx.y = sequence
@@ -397,17 +507,32 @@ __global__ __launch_bounds__(256) void gram_final_kernel(const unsigned char* pr
   }
 }
 
+// `slots` = B * tiles work units; with splits > 1 each is split along the
+// features and finished by gram_reduce_kernel from the partials in `part`
 template <class C>
-void launch_gram_max(const GramParams& p, int grid, int bf16, hipStream_t s) {
-  if (grid <= 0) return;
-  if (bf16) hipLaunchKernelGGL((gram_max_kernel<true, C>), dim3((unsigned)grid), dim3(C::NT), 0, s, p);
-  else hipLaunchKernelGGL((gram_max_kernel<false, C>), dim3((unsigned)grid), dim3(C::NT), 0, s, p);
+void launch_gram_max(GramParams p, int slots, int splits, float* part, int bf16, hipStream_t s) {
+  if (slots <= 0) return;
+  if (splits > 1) {
+    p.splits = splits;
+    p.part = part;
+    const dim3 grid((unsigned)(slots * splits));
+    if (bf16) hipLaunchKernelGGL((gram_max_kernel<true, C, true>), grid, dim3(C::NT), 0, s, p);
+    else hipLaunchKernelGGL((gram_max_kernel<false, C, true>), grid, dim3(C::NT), 0, s, p);
+    const long long threads = (long long)slots * C::KT * C::QT / 4;
+    hipLaunchKernelGGL((gram_reduce_kernel<C>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p,
+                       slots);
+  } else {
+    p.splits = 1;
+    if (bf16) hipLaunchKernelGGL((gram_max_kernel<true, C, false>), dim3((unsigned)slots), dim3(C::NT), 0, s, p);
+    else hipLaunchKernelGGL((gram_max_kernel<false, C, false>), dim3((unsigned)slots), dim3(C::NT), 0, s, p);
+  }
 }
 
-void launch_norms(const void* x, float* inv, int rows, int d, int bf16, hipStream_t s) {
+void launch_norms(const void* x, float* inv, int rows, int d, int bf16, hipStream_t s, int* mkey = nullptr,
+                  int* count = nullptr, int T = 1) {
   const dim3 grid((unsigned)((rows + 3) / 4));
-  if (bf16) hipLaunchKernelGGL(gram_norm_kernel<true>, grid, dim3(256), 0, s, x, inv, rows, d);
-  else hipLaunchKernelGGL(gram_norm_kernel<false>, grid, dim3(256), 0, s, x, inv, rows, d);
+  if (bf16) hipLaunchKernelGGL(gram_norm_kernel<true>, grid, dim3(256), 0, s, x, inv, rows, d, mkey, count, T);
+  else hipLaunchKernelGGL(gram_norm_kernel<false>, grid, dim3(256), 0, s, x, inv, rows, d, mkey, count, T);
 }
 
 }  // namespace
@@ -437,11 +562,16 @@ long long rect_tiles(int T) {
   return best;
 }
 
+// compute units of the current device (cached per device; 256 when the
+// runtime cannot say, e.g. with no device, which only sizes work splits)
 int cu_count() {
+  static int cached[64];
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
   return n;
 }
 
@@ -457,6 +587,24 @@ bool use_large_tiles(int B, int T) {
   return 16 * large < 10 * small;
 }
 
+// Fewer tiles than resident workgroups (short sequences): split each tile's
+// feature axis into up to (resident workgroups / tiles) ranges of at least
+// four stages, so the chip fills; the partial products are summed in a fixed
+// order afterwards.
+template <class C>
+int choose_splits(long long slots, int d) {
+  const long long resident = (long long)C::WG_PER_CU * cu_count();
+  if (slots <= 0 || slots >= resident) return 1;
+  const long long s = std::min<long long>(std::min<long long>(resident / slots, (d / KC) / 4), MAX_SPLITS);
+  return (int)std::max<long long>(1, s);
+}
+
+template <class C>
+size_t part_bytes(long long slots, int d) {
+  const int s = choose_splits<C>(slots, d);
+  return s > 1 ? (size_t)slots * s * C::KT * C::QT * sizeof(float) : 0;
+}
+
 int check_tokens(int B, int T, int d) {
   if (B < 1 || T < 1 || d < 64 || d > 65536 || d % 64) return ROPE_ATTN_ERR_SHAPE;
   if (T > (1 << 20) || (long long)T * d > (1LL << 31) || (long long)B * T > (1LL << 31))
@@ -470,14 +618,26 @@ bool mis4(const void* q) { return ((uintptr_t)q & 3u) != 0; }
 
 float gram_threshold(float tau) { return (float)(1.0 - (double)tau * (double)tau); }
 
-size_t select_bytes(int B, int T) {
-  const size_t n = (size_t)B * T;
-  return gup(4 * n) + gup(4 * n);  // inverse norms, running maxima
+size_t select_part_bytes(int B, int T, int d) {
+  return use_large_tiles(B, T) ? part_bytes<LargeTiles>(B * tri_tiles<LargeTiles>(T), d)
+                               : part_bytes<SmallTiles>(B * tri_tiles<SmallTiles>(T), d);
 }
 
-size_t cascade_bytes(int T) {
+size_t select_bytes(int B, int T, int d) {
+  const size_t n = (size_t)B * T;
+  // inverse norms, running maxima, split partial products
+  return gup(4 * n) + gup(4 * n) + gup(select_part_bytes(B, T, d));
+}
+
+size_t cascade_part_bytes(int T, int d) {
+  return std::max(part_bytes<SmallTiles>(tri_tiles<SmallTiles>(T), d),
+                  part_bytes<SmallTiles>(rect_tiles<SmallTiles>(T), d));
+}
+
+size_t cascade_bytes(int T, int d) {
   const size_t n = (size_t)T;
-  return gup(4 * n) + gup(4 * n) + gup(4 * n) + gup(4 * n) + gup(2 * 4) + gup(n);
+  return gup(4 * n) + gup(4 * n) + gup(4 * n) + gup(4 * n) + gup(2 * 4) + gup(n) +
+         gup(cascade_part_bytes(T, d));
 }
 
 int gram_finish() { return hipGetLastError() == hipSuccess ? ROPE_ATTN_OK : ROPE_ATTN_ERR_HIP; }
@@ -488,12 +648,12 @@ extern "C" {
 
 size_t gram_select_workspace_bytes(int B, int T, int d) {
   if (check_tokens(B, T, d)) return 0;
-  return select_bytes(B, T);
+  return select_bytes(B, T, d);
 }
 
 size_t gram_cascade_workspace_bytes(int T, int d) {
   if (check_tokens(1, T, d)) return 0;
-  return cascade_bytes(T);
+  return cascade_bytes(T, d);
 }
 
 int gram_select(const void* x, int B, int T, int d, int dtype, float tau, float* max_cos,
@@ -512,18 +672,17 @@ int gram_select_stages(unsigned stages, const void* x, int B, int T, int d, int 
   if (!(isfinite(tau) && tau >= 0.0f)) return ROPE_ATTN_ERR_ARG;
   if (mis16(x) || mis4(max_cos) || mis4(count) || ((uintptr_t)workspace & (GALIGN - 1)))
     return ROPE_ATTN_ERR_ALIGN;
-  if (workspace_bytes < select_bytes(B, T)) return ROPE_ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < select_bytes(B, T, d)) return ROPE_ATTN_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const size_t n = (size_t)B * T;
   char* ws = reinterpret_cast<char*>(workspace);
   float* inv = reinterpret_cast<float*>(ws);
   int* mkey = reinterpret_cast<int*>(ws + gup(4 * n));
+  float* part = reinterpret_cast<float*>(ws + 2 * gup(4 * n));
   const int bf16 = dtype == GRAM_BF16;
 
   if (stages & GRAM_STAGE_PREP) {
-    hipLaunchKernelGGL(gram_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, mkey,
-                       (int)n, count, B);
-    launch_norms(x, inv, (int)n, d, bf16, hs);
+    launch_norms(x, inv, (int)n, d, bf16, hs, mkey, count, T);
   }
   if (stages & GRAM_STAGE_GRAM) {
     GramParams p = {};
@@ -531,10 +690,12 @@ int gram_select_stages(unsigned stages, const void* x, int B, int T, int d, int 
     p.contiguous = 1;
     if (use_large_tiles(B, T)) {
       p.tiles = (int)tri_tiles<LargeTiles>(T);
-      launch_gram_max<LargeTiles>(p, B * p.tiles, bf16, hs);
+      const int slots = B * p.tiles;
+      launch_gram_max<LargeTiles>(p, slots, choose_splits<LargeTiles>(slots, d), part, bf16, hs);
     } else {
       p.tiles = (int)tri_tiles<SmallTiles>(T);
-      launch_gram_max<SmallTiles>(p, B * p.tiles, bf16, hs);
+      const int slots = B * p.tiles;
+      launch_gram_max<SmallTiles>(p, slots, choose_splits<SmallTiles>(slots, d), part, bf16, hs);
     }
   }
   if (stages & GRAM_STAGE_DECIDE)
@@ -553,7 +714,7 @@ int gram_cascade(const void* x, int T, int d, int dtype, float tau, const unsign
   if (!(isfinite(tau) && tau >= 0.0f)) return ROPE_ATTN_ERR_ARG;
   if (mis16(x) || mis4(max_cos) || mis4(count) || ((uintptr_t)workspace & (GALIGN - 1)))
     return ROPE_ATTN_ERR_ALIGN;
-  if (workspace_bytes < cascade_bytes(T)) return ROPE_ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < cascade_bytes(T, d)) return ROPE_ATTN_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const size_t n = (size_t)T;
   char* ws = reinterpret_cast<char*>(workspace);
@@ -563,6 +724,7 @@ int gram_cascade(const void* x, int T, int d, int dtype, float tau, const unsign
   int* idxN = reinterpret_cast<int*>(ws + 3 * gup(4 * n));
   int* cnt = reinterpret_cast<int*>(ws + 4 * gup(4 * n));
   unsigned char* valid = reinterpret_cast<unsigned char*>(ws + 4 * gup(4 * n) + gup(8));
+  float* part = reinterpret_cast<float*>(ws + 4 * gup(4 * n) + gup(8) + gup(n));
   const int bf16 = dtype == GRAM_BF16;
   const float thr = gram_threshold(tau);
 
@@ -576,7 +738,7 @@ int gram_cascade(const void* x, int T, int d, int dtype, float tau, const unsign
   p.qn = p.kn = cnt;
   p.tri = 1;
   p.tiles = (int)tri_tiles<SmallTiles>(T);
-  launch_gram_max<SmallTiles>(p, p.tiles, bf16, hs);
+  launch_gram_max<SmallTiles>(p, p.tiles, choose_splits<SmallTiles>(p.tiles, d), part, bf16, hs);
   hipLaunchKernelGGL(gram_valid_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, hs, idxR, cnt, mkey,
                      thr, valid);
   // the (T - r) x r product between the other tokens and the valid members
@@ -585,7 +747,7 @@ int gram_cascade(const void* x, int T, int d, int dtype, float tau, const unsign
   p.kvalid = valid;
   p.tri = 0;
   p.tiles = (int)rect_tiles<SmallTiles>(T);
-  launch_gram_max<SmallTiles>(p, p.tiles, bf16, hs);
+  launch_gram_max<SmallTiles>(p, p.tiles, choose_splits<SmallTiles>(p.tiles, d), part, bf16, hs);
   hipLaunchKernelGGL(gram_final_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, hs, prev, valid,
                      mkey, thr, max_cos, rep, count, T);
   return gram_finish();
