@@ -74,6 +74,9 @@ struct GramParams {
   int tri;                      // queries and keys are one list: lower-triangle tiles
   int tiles;                    // tiles per sequence in the grid (an upper bound)
   int splits;                   // feature-axis splits per tile (1: unsplit)
+  int sub_first;                // >= 0: ids are the 4 quarter tiles of large-tile triangle
+                                // ids sub_first, sub_first + 1, ... (sub_tiles per sequence)
+  int sub_tiles;
   float* part;                  // split partial products (splits > 1)
   int contiguous;               // hand each XCD a contiguous run of tiles (every id is real work)
 };
@@ -102,15 +105,38 @@ struct Frag<false> {
 template <class C>
 __device__ __forceinline__ bool decode_tile(const GramParams& p, int id, int splits, int& b, int& slot,
                                             int& q0, int& k0, int& split, int& nq, int& nk) {
+  nq = p.qn ? *p.qn : p.T;
+  nk = p.kn ? *p.kn : p.T;
+  int qt, kt;
+  if constexpr (LargeTiles::KT == 2 * C::KT && LargeTiles::QT == 2 * C::QT) {
+    if (p.sub_first >= 0) {
+      // quarter (id % 4) of large triangle tile sub_first + id / 4
+      typedef LargeTiles L;
+      const int big = p.sub_first + id / 4, quarter = id % 4;
+      b = big / p.sub_tiles;
+      const int tid = big - b * p.sub_tiles;
+      int lo = 0, hi = (p.T + L::QT - 1) / L::QT;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (L::tri_before(mid) <= tid) lo = mid;
+        else hi = mid;
+      }
+      qt = 2 * lo + (quarter >> 1);
+      kt = 2 * (tid - (int)L::tri_before(lo)) + (quarter & 1);
+      split = 0;
+      slot = id;
+      if (qt * C::QT >= nq || kt * C::KT >= nk) return false;
+      q0 = qt * C::QT;
+      k0 = kt * C::KT;
+      return k0 < min(q0 + C::QT, nq) - 1;  // identity lists (the full selection)
+    }
+  }
   const int per_seq = p.tiles * splits;
   b = id / per_seq;
   const int within = id - b * per_seq;
   const int tid = within / splits;
   split = within - tid * splits;
   slot = b * p.tiles + tid;
-  nq = p.qn ? *p.qn : p.T;
-  nk = p.kn ? *p.kn : p.T;
-  int qt, kt;
   if (p.tri) {
     // the largest qt with tri_before(qt) <= tid
     int lo = 0, hi = (p.T + C::QT - 1) / C::QT;
@@ -688,10 +714,24 @@ int gram_select_stages(unsigned stages, const void* x, int B, int T, int d, int 
     GramParams p = {};
     p.x = x; p.inv = inv; p.mkey = mkey; p.B = B; p.T = T; p.d = d; p.tri = 1;
     p.contiguous = 1;
+    p.sub_first = -1;
     if (use_large_tiles(B, T)) {
+      // whole rounds of resident large tiles; the large tiles left over for a
+      // last, mostly idle round run as four small tiles each instead
       p.tiles = (int)tri_tiles<LargeTiles>(T);
       const int slots = B * p.tiles;
-      launch_gram_max<LargeTiles>(p, slots, choose_splits<LargeTiles>(slots, d), part, bf16, hs);
+      const int resident = LargeTiles::WG_PER_CU * cu_count();
+      int full = slots / resident * resident;
+      // quarters of the leftover tiles fill at most one round of small tiles
+      if (full == 0 || 2 * (slots - full) > resident) full = slots;
+      launch_gram_max<LargeTiles>(p, full, 1, part, bf16, hs);
+      if (full < slots) {
+        GramParams q = p;
+        q.sub_first = full;
+        q.sub_tiles = p.tiles;
+        q.contiguous = 0;
+        launch_gram_max<SmallTiles>(q, 4 * (slots - full), 1, part, bf16, hs);
+      }
     } else {
       p.tiles = (int)tri_tiles<SmallTiles>(T);
       const int slots = B * p.tiles;
@@ -733,6 +773,7 @@ int gram_cascade(const void* x, int T, int d, int dtype, float tau, const unsign
   launch_norms(x, inv, T, d, bf16, hs);
   GramParams p = {};
   p.x = x; p.inv = inv; p.mkey = mkey; p.B = 1; p.T = T; p.d = d;
+  p.sub_first = -1;
   // the r x r product among the inherited members
   p.qidx = p.kidx = idxR;
   p.qn = p.kn = cnt;
