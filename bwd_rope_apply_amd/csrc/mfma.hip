@@ -35,6 +35,9 @@ namespace {
 #ifndef RA_DQ_BN
 #define RA_DQ_BN 32
 #endif
+#ifndef RA_DQ_SUB
+#define RA_DQ_SUB 2        // RA_DQ_BN-key products per copied tile (one barrier per tile)
+#endif
 #ifndef RA_DQ_WPS
 #define RA_DQ_WPS 2
 #endif
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
 // (transposed reads).
 template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
-  constexpr int KB = RA_DQ_BN, NMB = KB / 32;
+  constexpr int SB = RA_DQ_BN, NMB = SB / 32, KB = SB * RA_DQ_SUB;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, KB>::ALLOC;
   __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
@@ -406,9 +409,15 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
     }
     walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
-    if (!(CAUSAL && k0 > wrow0 + 31))
-      dq_tile<D, NMB, decltype(masked)::value>(acc, Ks + cur, Vs + cur, qf, df, k0, klim, lse2, dr,
-                                               lane);
+#pragma unroll
+    for (int sub = 0; sub < RA_DQ_SUB; ++sub) {
+      // rows SB sub .. of the tile: the row layout keeps each 32-row half whole
+      const int ks = k0 + SB * sub;
+      if (!(CAUSAL && ks > wrow0 + 31))
+        dq_tile<D, NMB, decltype(masked)::value>(acc, Ks + cur + SB * sub * (D + 8),
+                                                 Vs + cur + SB * sub * (D + 8), qf, df, ks, klim,
+                                                 lse2, dr, lane);
+    }
     wait_lds_copies();
     __syncthreads();
     walk.advance(kt);
