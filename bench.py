@@ -10,12 +10,15 @@ Throughput is algorithmic: 6 B H N^2 D flops per step (the two forward
 products and the four backward products over the causal half), the standard
 count for causal attention training; recomputation of scores in the backward
 is not counted (the FlashAttention convention, which adds it, 7 B H N^2 D, is
-reported beside it).  Per-stage durations come from HIP events recorded on
-the stream the library launches on (torch's current stream), between the
-staged entry points, so the timed work is exactly the full forward +
-backward.  One workspace serves both passes: the backward reuses the
-forward's rotated fp16 planes and frequency table (saved activations) and
-prepares only dO and D.
+reported beside it).  Durations come from HIP events recorded on the stream
+the library launches on (torch's current stream), between the staged entry
+points: the timed step is the forward in one call and the backward in three
+(the dK/dV kernel alone in one of them, for the roofline), so the timed work
+is exactly the full forward + backward.  A few untimed steps afterwards run
+every kernel in its own call for the per-kernel breakdown (stages_ms_serial).
+One workspace serves both passes: the backward reuses the forward's rotated
+fp16 planes and frequency table (saved activations) and prepares only dO
+and D.
 
 --gram times Gram-threshold token selection instead (see bench_gram).
 
@@ -36,14 +39,20 @@ PEAK_TFLOPS = 2516.6   # fp16 / bf16 dense matrix cores: 256 CU x 2.4 GHz x 4096
 HBM_GBS = 8000.0
 METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
 
+# The timed step: the whole forward in one call (its exact-corner kernel
+# runs beside the main kernel), the backward in three calls, split where a
+# kernel is timed on its own: prep (PREP_GRAD: only dO and D, reusing the
+# forward's table and operand planes from the shared workspace), corner and
+# dQ (the corner kernels beside dQ); dK/dV; the d alpha reduction.
+FWD_CALLS = [("fwd", 1 | 2 | 4)]
+BWD_CALLS = [("bwd_prep_exact_dq", 64 | 2 | 8), ("bwd_dkdv", 16), ("bwd_dalpha", 32)]
+# every kernel in its own call (serial), timed after the timed step for the breakdown
 FWD_STAGES = [("fwd_prep", 1), ("fwd_exact", 2), ("fwd_main", 4)]
-# the backward reuses the forward's table and operand planes from the shared
-# workspace (PREP_GRAD: it converts only dO and computes D)
 BWD_STAGES = [("bwd_prep", 64), ("bwd_exact", 2), ("bwd_dq", 8), ("bwd_dkdv", 16),
               ("bwd_dalpha", 32)]
-# algorithmic products carried by each matrix-core stage (units of B H N^2 D
-# flops, causal): fwd QK^T and PV; dQ; dV, dP and dK
-STAGE_FLOP_UNITS = {"fwd_main": 2.0, "bwd_dq": 1.0, "bwd_dkdv": 3.0}
+# algorithmic products of the dominant matrix-core kernel (units of B H N^2 D
+# flops, causal): dV, dP and dK
+DOMINANT = ("bwd_dkdv", "dkdv_kernel", 3.0)
 
 
 def parse():
@@ -312,15 +321,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(events=None):
+    def step(fwd_calls, bwd_calls, events=None):
         i = 0
-        for name, bit in FWD_STAGES:
+        for name, bit in fwd_calls:
             if events is not None:
                 events[i].record()
             _lib.fwd(q, k, v, wl.base, alpha, wl.causal, workspace=ws_f, out=(o, lse), stages=bit,
                      opts=opts)
             i += 1
-        for name, bit in BWD_STAGES:
+        for name, bit in bwd_calls:
             if events is not None:
                 events[i].record()
             _lib.bwd(q, k, v, o, do, lse, wl.base, alpha, wl.causal, workspace=ws_b,
@@ -329,15 +338,16 @@ def main():
         if events is not None:
             events[i].record()
 
+    calls = [n for n, _ in FWD_CALLS] + [n for n, _ in BWD_CALLS]
     for _ in range(args.warmup):
-        step()
+        step(FWD_CALLS, BWD_CALLS)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(ev[s])
+        step(FWD_CALLS, BWD_CALLS, ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if not (torch.isfinite(o).all() and torch.isfinite(dq).all() and torch.isfinite(dk).all()
@@ -345,22 +355,28 @@ def main():
         print("bench.py: non-finite outputs", file=sys.stderr)
         sys.exit(1)
 
-    stage_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
-                for i, n in enumerate(names)}
-    nf = len(FWD_STAGES)
-    step_ev = np.array([ev[s][0].elapsed_time(ev[s][len(names)]) for s in range(args.steps)])
+    call_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+               for i, n in enumerate(calls)}
+    nf = len(FWD_CALLS)
+    step_ev = np.array([ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(args.steps)])
     fwd_ev = np.array([ev[s][0].elapsed_time(ev[s][nf]) for s in range(args.steps)])
-    bwd_ev = np.array([ev[s][nf].elapsed_time(ev[s][len(names)]) for s in range(args.steps)])
+    bwd_ev = np.array([ev[s][nf].elapsed_time(ev[s][len(calls)]) for s in range(args.steps)])
+    # per-kernel breakdown: every kernel in its own call (no overlap), after the timed steps
+    nd = min(args.steps, 5)
+    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nd)]
+    for s in range(nd):
+        step(FWD_STAGES, BWD_STAGES, evd[s])
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([evd[s][i].elapsed_time(evd[s][i + 1]) for s in range(nd)]))
+                for i, n in enumerate(names)}
     ms_step = wall * 1e3 / args.steps
     unit = 2.0 * pairs * D
     flops = 6.0 * unit
     value = flops / (ms_step * 1e-3) / 1e12
 
-    dom = max(STAGE_FLOP_UNITS, key=lambda n: stage_ms[n])
-    dom_flops = STAGE_FLOP_UNITS[dom] * unit
-    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    dom, kernel, dom_units = DOMINANT
+    achieved = dom_units * unit / (call_ms[dom] * 1e-3) / 1e12
     traffic = measured_traffic(args.traffic, dom) if args.retrieved < 0 else None
-    kernel = {"fwd_main": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}[dom]
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -380,8 +396,9 @@ def main():
                    "flops_per_step": flops, "pct_bf16_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": traffic, "avg_ms": round(stage_ms[dom], 4)},
-        "stages_ms": {n: round(t, 4) for n, t in stage_ms.items()},
+                     "traffic": traffic, "avg_ms": round(call_ms[dom], 4)},
+        "calls_ms": {n: round(t, 4) for n, t in call_ms.items()},
+        "stages_ms_serial": {n: round(t, 4) for n, t in stage_ms.items()},
         "events_ms": {"step_median": round(float(np.median(step_ev)), 4),
                       "step_min": round(float(step_ev.min()), 4),
                       "fwd_median": round(float(np.median(fwd_ev)), 4),
