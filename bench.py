@@ -84,10 +84,17 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_SOURCES = ("mfma.hip", "tile.h", "common.h")
+
+
 def kernel_source_hash() -> str:
+    """sha256 over the sources of the MFMA attention kernels, in order."""
     import hashlib
-    with open(os.path.join(ROOT, "bwd_rope_apply_amd", "csrc", "mfma.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bwd_rope_apply_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(path: str, stage: str):
