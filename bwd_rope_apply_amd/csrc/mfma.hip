@@ -153,7 +153,8 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const hal
   const int l32 = lane & 31, g = lane >> 5;
   f32x16 s[NMB], dp[NMB];
   scores<D, NMB>(s, Ks, qf, l32, g, -lse2);
-  scores<D, NMB>(dp, Vs, df, l32, g, -dr);
+  // P first: it needs only the scores, so its exps can issue between the
+  // dP products
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -163,8 +164,14 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const hal
         const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7);
         pr = key > klim ? 0.f : pr;
       }
-      s[mb][r] = pr * dp[mb][r];
+      s[mb][r] = pr;
     }
+  }
+  scores<D, NMB>(dp, Vs, df, l32, g, -dr);
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[mb][r] *= dp[mb][r];
   }
   half8 sf[2 * NMB];
   to_frags<NMB>(s, sf);
@@ -183,6 +190,26 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
   const int l32 = lane & 31, g = lane >> 5;
   f32x16 s[NMB], dp[NMB];
   scores<D, NMB>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
+  // P first: it needs only the scores, so its exps can issue between the
+  // dP products below
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ql = 32 * mb + 16 * h + 8 * g;
+      const float* lr = rsc + 64 * mb + 16 * h + 8 * g;
+      const float4 la = *reinterpret_cast<const float4*>(lr);
+      const float4 lb = *reinterpret_cast<const float4*>(lr + 4);
+      const float lv8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * h + e;
+        float pr = exp2_fast(s[mb][r] - lv8[e]);
+        if (MASK) pr = key > r0 + ql + e ? 0.f : pr;
+        s[mb][r] = pr;
+      }
+    }
+  }
   {
     half8 vl[D / 16];
 #pragma unroll
@@ -193,21 +220,14 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int ql = 32 * mb + 16 * h + 8 * g;
       const float* lr = rsc + 64 * mb + 16 * h + 8 * g;
-      const float4 la = *reinterpret_cast<const float4*>(lr);
-      const float4 lb = *reinterpret_cast<const float4*>(lr + 4);
       const float4 da = *reinterpret_cast<const float4*>(lr + 32);
       const float4 db = *reinterpret_cast<const float4*>(lr + 36);
-      const float lv8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
       const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * h + e;
-        float pr = exp2_fast(s[mb][r] - lv8[e]);
-        if (MASK) pr = key > r0 + ql + e ? 0.f : pr;
-        s[mb][r] = pr;
-        dp[mb][r] = pr * (dp[mb][r] - dv8[e]);
+        dp[mb][r] = s[mb][r] * (dp[mb][r] - dv8[e]);
       }
     }
   }
