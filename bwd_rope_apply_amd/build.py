@@ -18,6 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librope_attn.so")
+EXAMPLE = os.path.join(HERE, "rope_attn_example")
 SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "corner.hip", "gram.hip"]
 ARCH = "gfx950"
 
@@ -48,8 +49,16 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the plain C++ caller of the C ABI (examples/), linked against the library
+    ex_src = os.path.join(HERE, "examples", "rope_attn_example.cpp")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O2", "-std=c++17", f"-I{INCLUDE}", ex_src, f"-L{HERE}",
+           "-lrope_attn", "-Wl,-rpath,$ORIGIN", "-o", EXAMPLE + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"example build failed:\n{r.stderr}")
+    os.replace(EXAMPLE + ".tmp", EXAMPLE)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {EXAMPLE}")
     return LIB
 
 

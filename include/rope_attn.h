@@ -2,7 +2,7 @@
  * rope_attn.h -- exact softmax attention with rotary position embedding and
  * learnable per-band log-frequencies, forward and backward, on AMD gfx950.
  *
- * What is computed (all four entry points share these conventions):
+ * What is computed (every entry point shares these conventions):
  *
  *   theta_m     = base^(-2m/D),  theta_hat_m = exp(alpha_m) * theta_m,
  *                 m = 0 .. D/2-1  (LeRoPE, "Central mechanism"; alpha = 0 is
@@ -46,9 +46,15 @@
  * returns ROPE_ATTN_ERR_HIP.
  *
  * Numerics: with bf16 inputs, products run on fp16 matrix-core operands with
- * float32 accumulation, except the leading causal corner (query rows < 128)
- * which, like every call with fp32 inputs, runs in float32 throughout.  The
- * fp16 operands require |Q|, |K|, |V|, |dO| entries below 6.5e4.
+ * float32 accumulation, except the leading causal corner (query rows below
+ * 128 per started 8192 positions; one 128-row block with block lists), whose
+ * products use split fp16 operands (hi + lo, three products per
+ * contraction, about 22-bit operands) with float32 accumulation.  Calls with
+ * fp32 inputs run in float32 throughout.  The fp16 operands require |Q|,
+ * |K|, |V|, |dO| entries below 6.5e4.
+ *
+ * bwd_rope_apply_amd/examples/rope_attn_example.cpp is a plain C++ caller of
+ * these entry points (one problem from a file, forward and backward). */
  */
 #ifndef ROPE_ATTN_H
 #define ROPE_ATTN_H
