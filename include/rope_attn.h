@@ -54,7 +54,7 @@
  * |K|, |V|, |dO| entries below 6.5e4.
  *
  * bwd_rope_apply_amd/examples/rope_attn_example.cpp is a plain C++ caller of
- * these entry points (one problem from a file, forward and backward). */
+ * these entry points (one problem from a file, forward and backward).
  */
 #ifndef ROPE_ATTN_H
 #define ROPE_ATTN_H
