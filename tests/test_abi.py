@@ -170,3 +170,23 @@ def test_gram_select_validation(lib, args, status):
 ])
 def test_gram_cascade_validation(lib, args, status):
     assert lib.gram_cascade(*args) == status
+
+
+def test_headers_compile_as_plain_c(tmp_path):
+    """Both headers are C: a C99 translation unit that includes them and
+    takes the address of every declared function compiles without warnings."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use.c"
+    names = _declared()
+    src.write_text('#include "rope_attn.h"\n#include "gram_select.h"\n'
+                   "typedef void (*fn)(void);\n"
+                   "fn table[] = {" + ", ".join(f"(fn)&{n}" for n in names) + "};\n"
+                   "int main(void) { return table[0] == 0; }\n")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        f"-I{os.path.join(ROOT, 'include')}", "-c", str(src), "-o", str(tmp_path / "use.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
