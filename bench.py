@@ -108,16 +108,35 @@ def measured_traffic(path: str, stage: str):
     return t.get("bytes_per_launch", {}).get(stage)
 
 
+def host_blas():
+    """(threads, BLAS library) of numpy's thread pool on this host."""
+    import numpy  # noqa: F401  (loads the BLAS that threadpoolctl then reports)
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        lib = ",".join(sorted({str(i.get("internal_api", "?")) for i in info})) or "?"
+        return int(threads), lib
+    except Exception:  # threadpoolctl is optional
+        return len(os.sched_getaffinity(0)), "?"
+
+
+def device_info():
+    """CU count and name of cuda:0, and the dense fp16/bf16 matrix peak
+    recomputed from the CU count at the 2.4 GHz the published peak uses."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    cus = int(props.multi_processor_count)
+    return {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", "?"), "cus": cus,
+            "peak_fp16_tflops_at_2p4ghz": round(cus * 4 * 1024 * 2.4e9 / 1e12, 1)}
+
+
 def cpu_baseline(inp, wl):
     """The float64 oracle on one head of the same inputs (a bounded sample),
     timed on the host cores, scaled to TFLOP/s with the same flop count."""
     import numpy as np
     from oracle import ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+    threads, blas = host_blas()
     full = {n: inp.f64(n).reshape(-1, 1, wl.N, wl.D) for n in ("q", "k", "v", "do")}
 
     def run(heads):
@@ -134,7 +153,8 @@ def cpu_baseline(inp, wl):
     flops = 6.0 * heads * wl.N * wl.N * wl.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of {wl.B * wl.H} heads (N={wl.N}, D={wl.D}), float64 fwd+bwd incl. "
-                      f"dalpha, {dt:.1f} s"}
+                      f"dalpha, {dt:.1f} s", "blas": blas,
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def visible_pairs(lists, N: int, causal: bool) -> int:
@@ -161,11 +181,7 @@ def gram_cpu_baseline(x, tau, d):
     bounded sample of the same workload), timed on the host cores."""
     import numpy as np
     from oracle import gram
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+    threads, blas = host_blas()
     Ts = min(x.shape[0], 2048)
     xs = np.ascontiguousarray(x[:Ts])
     t0 = time.perf_counter()
@@ -173,7 +189,7 @@ def gram_cpu_baseline(x, tau, d):
     dt = time.perf_counter() - t0
     return {"value": d * Ts * (Ts - 1) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": f"first {Ts} of {x.shape[0]} tokens (d={d}), float64 "
-                                        f"selection, {dt:.2f} s"}
+                                        f"selection, {dt:.2f} s", "blas": blas}
 
 
 def bench_gram(args):
@@ -413,6 +429,7 @@ def main():
         "tflops_fwd": round(2.0 * unit / (float(np.median(fwd_ev)) * 1e-3) / 1e12, 2),
         "tflops_bwd": round(4.0 * unit / (float(np.median(bwd_ev)) * 1e-3) / 1e12, 2),
         "tflops_fa_convention": round(7.0 * unit / (ms_step * 1e-3) / 1e12, 2),
+        "device": device_info(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, wl)
