@@ -12,7 +12,7 @@ count for causal attention training; recomputation of scores in the backward
 is not counted (the FlashAttention convention, which adds it, 7 B H N^2 D, is
 reported beside it).  Durations come from HIP events recorded on the stream
 the library launches on (torch's current stream), between the staged entry
-points: the timed step is the forward in one call and the backward in three
+points: the timed step is the forward in one call and the backward in four
 (the dK/dV kernel alone in one of them, for the roofline), so the timed work
 is exactly the full forward + backward.  A few untimed steps afterwards run
 every kernel in its own call for the per-kernel breakdown (stages_ms_serial).
@@ -39,17 +39,20 @@ PEAK_TFLOPS = 2516.6   # fp16 / bf16 dense matrix cores: 256 CU x 2.4 GHz x 4096
 HBM_GBS = 8000.0
 METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
 
-# The timed step: the whole forward in one call (its exact-corner kernel
-# runs beside the main kernel), the backward in three calls, split where a
-# kernel is timed on its own: prep (PREP_GRAD: only dO and D, reusing the
-# forward's table and operand planes from the shared workspace), corner and
-# dQ (the corner kernels beside dQ); dK/dV; the d alpha reduction.
-FWD_CALLS = [("fwd", 1 | 2 | 4)]
-BWD_CALLS = [("bwd_prep_exact_dq", 64 | 2 | 8), ("bwd_dkdv", 16), ("bwd_dalpha", 32)]
+# Stage bits of the C ABI (rope_attn_stage)
+PREP, EXACT, MAIN, DKDV, DQ, DALPHA, PREP_GRAD = 1, 2, 4, 8, 16, 32, 64
+# The timed step: the whole forward in one call, the backward in four calls,
+# split where a kernel is timed on its own: prep (PREP_GRAD: only dO and D,
+# reusing the forward's table and operand planes from the shared workspace)
+# and the exact corner; dK/dV (which also writes the dS panels); dQ (from
+# the panels); the d alpha reduction.
+FWD_CALLS = [("fwd", PREP | EXACT | MAIN)]
+BWD_CALLS = [("bwd_prep_exact", PREP_GRAD | EXACT), ("bwd_dkdv", DKDV), ("bwd_dq", DQ),
+             ("bwd_dalpha", DALPHA)]
 # every kernel in its own call (serial), timed after the timed step for the breakdown
-FWD_STAGES = [("fwd_prep", 1), ("fwd_exact", 2), ("fwd_main", 4)]
-BWD_STAGES = [("bwd_prep", 64), ("bwd_exact", 2), ("bwd_dq", 8), ("bwd_dkdv", 16),
-              ("bwd_dalpha", 32)]
+FWD_STAGES = [("fwd_prep", PREP), ("fwd_exact", EXACT), ("fwd_main", MAIN)]
+BWD_STAGES = [("bwd_prep", PREP_GRAD), ("bwd_exact", EXACT), ("bwd_dkdv", DKDV), ("bwd_dq", DQ),
+              ("bwd_dalpha", DALPHA)]
 # algorithmic products of the dominant matrix-core kernel (units of B H N^2 D
 # flops, causal): dV, dP and dK
 DOMINANT = ("bwd_dkdv", "dkdv_kernel", 3.0)
@@ -72,6 +75,8 @@ def parse():
     ap.add_argument("--retrieved", type=int, default=-1,
                     help="block-list attention: key blocks retrieved per 128-row query block "
                          "(seeded, uniform among the blocks it may see); -1 = dense")
+    ap.add_argument("--min-workspace", action="store_true",
+                    help="the smallest backward workspace: no dS panels, dQ recomputes the scores")
     ap.add_argument("--gram", action="store_true",
                     help="time Gram-threshold token selection (and one cascade step) instead")
     ap.add_argument("--gram-workload", default="gram_8k")
@@ -316,7 +321,9 @@ def main():
     da = torch.empty((D // 2,), **f32)
     dt_code = _lib.BF16 if wl.dtype == "bf16" else _lib.FP32
     # one buffer for both passes (the forward's regions are a prefix of the backward's)
-    ws_b = torch.empty(_lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal), dtype=torch.uint8, device=dev)
+    ws_kind = "bwd_min" if args.min_workspace else "bwd"
+    ws_b = torch.empty(_lib.workspace_bytes(ws_kind, B, H, N, D, dt_code, wl.causal), dtype=torch.uint8,
+                       device=dev)
     ws_f = ws_b
 
     names = [n for n, _ in FWD_STAGES] + [n for n, _ in BWD_STAGES]
@@ -416,6 +423,10 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
                    "base": wl.base, "storage": wl.dtype, "outputs": "fp32",
                    "options": opts_config,
+                   "dq_pass": ("recompute" if args.min_workspace or args.retrieved >= 0
+                               or _lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal)
+                               == _lib.workspace_bytes("bwd_min", B, H, N, D, dt_code, wl.causal)
+                               else "ds_panels"),
                    "flops_per_step": flops, "pct_bf16_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "librope_attn.so")
 
 FP32, BF16 = 0, 1
 # rope_attn_stage bits
-STAGE_PREP, STAGE_EXACT, STAGE_MAIN, STAGE_DQ, STAGE_DKDV, STAGE_DALPHA = 1, 2, 4, 8, 16, 32
+STAGE_PREP, STAGE_EXACT, STAGE_MAIN, STAGE_DKDV, STAGE_DQ, STAGE_DALPHA = 1, 2, 4, 8, 16, 32
 STAGE_ALL = 63
 STAGE_PREP_GRAD = 64   # backward: dO plane and D only, reusing the forward's workspace
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.rope_attn_fwd_workspace_bytes.restype = sz
     lib.rope_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.rope_attn_bwd_workspace_bytes.restype = sz
+    lib.rope_attn_bwd_workspace_bytes_min.argtypes = [i, i, i, i, i, i]
+    lib.rope_attn_bwd_workspace_bytes_min.restype = sz
     lib.rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, vp, i, vp, sz, vp]
     lib.rope_attn_fwd.restype = i
     lib.rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, vp, i,
@@ -165,8 +167,11 @@ def _alpha(alpha, q, D):
 
 
 def workspace_bytes(kind: str, B: int, H: int, N: int, D: int, dtype: int, causal: bool) -> int:
+    """kind "fwd", "bwd" (with the dS panels where they apply) or "bwd_min"
+    (the smallest backward workspace: dQ recomputes the scores)."""
     lib = load()
-    f = lib.rope_attn_fwd_workspace_bytes if kind == "fwd" else lib.rope_attn_bwd_workspace_bytes
+    f = {"fwd": lib.rope_attn_fwd_workspace_bytes, "bwd": lib.rope_attn_bwd_workspace_bytes,
+         "bwd_min": lib.rope_attn_bwd_workspace_bytes_min}[kind]
     return int(f(B, H, N, D, dtype, int(causal)))
 
 

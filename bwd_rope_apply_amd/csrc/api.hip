@@ -25,6 +25,10 @@ struct Shape {
   int corner() const { return (bf16() && causal) ? (blocks ? BLK : corner_rows(N)) : 0; }
   // block visibility bitmask (any call that may use block lists)
   bool mask_ok() const { return N <= MAX_BLOCKS * BLK; }
+  // dS panels for the backward's dQ product (bf16, up to PANEL_MAX_BYTES)
+  size_t panel_bytes() const { return 2 * bh() * panel_head(N, causal); }
+  bool panels_ok() const { return bf16() && panel_bytes() <= PANEL_MAX_BYTES; }
+  static constexpr size_t PANEL_MAX_BYTES = (size_t)16 << 30;
 };
 
 int check_shape(const Shape& s) {
@@ -81,11 +85,13 @@ int resolve(const rope_attn_options* o, const Shape& s, Opts& r) {
 // The forward's regions (table, operand planes, corner low parts) come first
 // and are laid out identically by both passes, so a backward run on the
 // forward's workspace can reuse them (ROPE_ATTN_STAGE_PREP_GRAD).
+// The dS panels come last, so the layouts with and without them agree on
+// every other region.
 struct Layout {
-  size_t theta, cs, qh, kh, vh, qlo, klo, bmask, doh, drow, rs, dkp, dvp, part;
+  size_t theta, cs, qh, kh, vh, qlo, klo, bmask, doh, drow, rs, dkp, dvp, part, dsp;
   int slots;
   size_t total() const {
-    return theta + cs + qh + kh + vh + qlo + klo + bmask + doh + drow + rs + dkp + dvp + part;
+    return theta + cs + qh + kh + vh + qlo + klo + bmask + doh + drow + rs + dkp + dvp + part + dsp;
   }
 };
 
@@ -100,15 +106,18 @@ MfmaParams mfma_base(const Shape& s, float scale) {
 }
 
 // dQ/dK/dV/dalpha partial-sum slots of the MFMA path for one corner choice
-int mfma_slots(const Shape& s) {
-  const MfmaParams m = mfma_base(s, 1.0f);
+// and dQ kernel (panels or recomputation)
+int mfma_slots(const Shape& s, bool panels) {
+  MfmaParams m = mfma_base(s, 1.0f);
+  if (panels) m.dsp = reinterpret_cast<half_t*>(ALIGN);  // only selects the dQ kernel's grid
   return (s.corner() ? corner_dq_slots(m) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
 }
 
 // Region sizes do not depend on whether a call passes block lists (the
 // workspace queries take no options): corner regions are sized for the
-// larger, dense corner, and the slot count is the larger of the two.
-Layout layout(Shape s, bool bwd) {
+// larger, dense corner, and the slot count is the largest over the modes.
+// `panels` adds the backward's dS panels (only when s.panels_ok()).
+Layout layout(Shape s, bool bwd, bool panels = false) {
   Layout L = {};
   s.blocks = 0;
   L.theta = up(sizeof(double) * (s.D / 2));
@@ -127,12 +136,13 @@ Layout layout(Shape s, bool bwd) {
     if (s.bf16()) {
       Shape sb = s;
       sb.blocks = 1;
-      L.slots = mfma_slots(s);
-      if (s.mask_ok()) L.slots = max(L.slots, mfma_slots(sb));
+      L.slots = max(mfma_slots(s, false), mfma_slots(s, true));
+      if (s.mask_ok()) L.slots = max(L.slots, mfma_slots(sb, false));
     } else {
       L.slots = 2 * simt_slots((int)s.bh(), s.N);
     }
     L.part = up(sizeof(float) * (size_t)L.slots * (s.D / 2));
+    if (panels && s.panels_ok()) L.dsp = up(s.panel_bytes());
   }
   return L;
 }
@@ -198,7 +208,13 @@ size_t rope_attn_fwd_workspace_bytes(int B, int H, int N, int D, int dtype, int 
 size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal) {
   const Shape s{B, H, N, D, dtype, causal};
   if (check_shape(s)) return 0;
-  return layout(s, true).total();
+  return layout(s, true, true).total();
+}
+
+size_t rope_attn_bwd_workspace_bytes_min(int B, int H, int N, int D, int dtype, int causal) {
+  const Shape s{B, H, N, D, dtype, causal};
+  if (check_shape(s)) return 0;
+  return layout(s, true, false).total();
 }
 
 int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void* q, const void* k,
@@ -299,7 +315,11 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   if (st) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const Layout L = layout(s, true);
+  // dQ as a product over dS panels when the workspace holds them (dense
+  // attention), else by recomputing the scores
+  const Layout Lp = layout(s, true, true);
+  const bool panels = !op.bptr && Lp.dsp && workspace_bytes >= Lp.total();
+  const Layout L = panels ? Lp : layout(s, true, false);
   Carve c{reinterpret_cast<char*>(workspace)};
   double* theta = c.take<double>(L.theta);
   float2* cs = c.take<float2>(L.cs);
@@ -315,10 +335,12 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   float* dkp = c.take<float>(L.dkp);
   float* dvp = c.take<float>(L.dvp);
   float* part = c.take<float>(L.part);
+  half_t* dsp = c.take<half_t>(L.dsp);
 
   // d alpha partial slots: [exact or corner dQ rows | exact dK rows | MFMA dQ | MFMA dK]
   const int BHi = (int)s.bh();
   MfmaParams mp = mfma_base(s, op.scale);
+  mp.dsp = dsp;
   const int n_exact_dq = s.bf16() ? (s.corner() ? corner_dq_slots(mp) : 0) : simt_slots(BHi, N);
   const int n_exact_dk = s.bf16() ? 0 : simt_slots(BHi, N);
   const int n_dq = s.bf16() ? dq_mfma_slots(mp) : 0;
@@ -362,13 +384,14 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       launch_corner_dkdv(mp, hs);  // rotated-frame partials, no d alpha slots
     }
   }
-  if ((stages & ROPE_ATTN_STAGE_DQ) && s.bf16()) {
-    mp.slot0 = n_exact_dq + n_exact_dk;
-    launch_dq_mfma(mp, hs);
-  }
+  // dK/dV first: with panels it writes the dS that the dQ product reads
   if ((stages & ROPE_ATTN_STAGE_DKDV) && s.bf16()) {
     mp.slot0 = n_exact_dq + n_exact_dk + n_dq;
     launch_dkdv_mfma(mp, hs);
+  }
+  if ((stages & ROPE_ATTN_STAGE_DQ) && s.bf16()) {
+    mp.slot0 = n_exact_dq + n_exact_dk;
+    launch_dq_mfma(mp, hs);
   }
   if ((stages & ROPE_ATTN_STAGE_DALPHA) && dalpha) {
     DalphaParams dp = {};
@@ -403,7 +426,7 @@ const char* rope_attn_status_string(int status) {
     case ROPE_ATTN_ERR_SHAPE: return "invalid shape: need B, H, N >= 1 and D in {64, 128}";
     case ROPE_ATTN_ERR_DTYPE: return "dtype must be ROPE_ATTN_FP32 or ROPE_ATTN_BF16";
     case ROPE_ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
-    case ROPE_ATTN_ERR_WORKSPACE: return "workspace smaller than the *_workspace_bytes query";
+    case ROPE_ATTN_ERR_WORKSPACE: return "workspace smaller than the *_workspace_bytes(_min) query";
     case ROPE_ATTN_ERR_HIP: return "HIP runtime reported a launch error";
     case ROPE_ATTN_ERR_ARG:
       return "base must be finite and > 0, causal 0 or 1; options: unrotated_pairs in [0, D/2], "

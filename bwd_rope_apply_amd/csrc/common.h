@@ -42,6 +42,30 @@ constexpr int MAX_BLOCKS = 512;
 __host__ __device__ inline int n_blocks(int N) { return (N + BLK - 1) / BLK; }
 __host__ __device__ inline int mask_words(int N) { return (n_blocks(N) + 31) / 32; }
 
+// dS panels (bf16 backward with a large enough workspace): the dK/dV pass
+// stores dS of every head in fp16, one panel per PANEL-query block; the dQ
+// pass reads them as the left operand of dQ~ = dS K~.  Under the causal mask
+// panel b holds keys 0 .. PANEL (b + 1) - 1 (the rest are masked), otherwise
+// every key up to PANEL n_panels(N).  A panel is blocked by 32 keys x 32
+// queries, 2 KiB per block, blocks ordered [key block][query block]; inside
+// a block, element (key k, query q) sits at half (q / 16) 512 + k 16 + q % 16.
+// One wave's dK/dV step (32 keys x 32 queries) is then one contiguous block,
+// stored by two fully coalesced 1 KiB instructions, and 32 keys of a panel
+// are one contiguous 16 KiB tile.  Offsets are in halfs from the head's
+// first panel.
+constexpr int PANEL = 256;
+__host__ __device__ inline int n_panels(int N) { return (N + PANEL - 1) / PANEL; }
+__host__ __device__ inline int panel_rows(int b, int N, int causal) {
+  return causal ? PANEL * (b + 1) : PANEL * n_panels(N);
+}
+__host__ __device__ inline size_t panel_off(int b, int N, int causal) {
+  return causal ? (size_t)PANEL * PANEL * ((size_t)b * (b + 1) / 2)
+                : (size_t)b * PANEL * ((size_t)PANEL * n_panels(N));
+}
+__host__ __device__ inline size_t panel_head(int N, int causal) {
+  return panel_off(n_panels(N), N, causal);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -113,6 +137,7 @@ struct MfmaParams {
   float* o; float* out_lse;
   float* dq; float* dk; float* dv;
   float* dk_part; float* dv_part;   // corner partials [BH][corner][D] or null
+  half_t* dsp;                      // dS panels [BH][panel_head] (dK/dV writes, dQ reads), or null
   float* dalpha_part;
   int slot0;
   const uint32_t* bmask;           // block visibility [BH][nb][W], or null (causal triangle / all)
@@ -142,7 +167,7 @@ int simt_slots(int BH, int rows);       // dalpha slots used by one simt dq/dkdv
 void launch_fwd_mfma(const MfmaParams& p, hipStream_t s);
 void launch_dq_mfma(const MfmaParams& p, hipStream_t s);
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);
-int dq_mfma_slots(const MfmaParams& p);
+int dq_mfma_slots(const MfmaParams& p);   // either dQ kernel (p.dsp selects)
 int dkdv_mfma_slots(const MfmaParams& p);
 void launch_corner_fwd(const MfmaParams& p, hipStream_t s);
 void launch_corner_dq(const MfmaParams& p, hipStream_t s);

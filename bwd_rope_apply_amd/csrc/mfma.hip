@@ -182,11 +182,14 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const hal
 // along n): P = exp(S - LSE), dV += P^T dO, dP = dO V^T, dS = P o (dP - D),
 // dK~ += dS^T Q~.  MASK hides queries before this lane's key.  rsc holds
 // the step's row scalars, 32-row groups of [LSE * log2(e) | D]; vrow points
-// at this lane's V row in the stationary LDS tile.
-template <int D, int NMB, bool MASK>
+// at this lane's V row in the stationary LDS tile.  DS also hands out the
+// fp16 dS row of this lane's key (its 32 NMB queries, 8 per 16-byte chunk)
+// in ds_out, zeros for a key at or past N.
+template <int D, int NMB, bool MASK, bool DS = false>
 __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* Qs,
                                           const half_t* Ds, const float* rsc, const half8* kf,
-                                          const half_t* vrow, int r0, int key, int lane) {
+                                          const half_t* vrow, int r0, int key, int lane,
+                                          half8* ds_out = nullptr, bool key_ok = true) {
   const int l32 = lane & 31, g = lane >> 5;
   f32x16 s[NMB], dp[NMB];
   scores<D, NMB>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
@@ -234,6 +237,10 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
   half8 pf[2 * NMB], sf[2 * NMB];
   to_frags<NMB>(s, pf);
   to_frags<NMB>(dp, sf);
+  if constexpr (DS) {
+#pragma unroll
+    for (int t = 0; t < 2 * NMB; ++t) ds_out[t] = key_ok ? sf[t] : half8{};
+  }
   accumulate_tr<D, 2 * NMB>(dv, Ds, pf, lane);
   accumulate_tr<D, 2 * NMB>(dk, Qs, sf, lane);
 }
@@ -460,8 +467,10 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
 // Workgroup = 128 keys of one head (4 waves x 32 keys); streams QB-row
 // tiles of Q~ and dO plus their row scalars.  Q~ serves the score product
 // and dK~ += dS^T Q~; dO serves dP = dO V^T and dV += P^T dO.  The
-// workgroup's V rows stay in LDS (natural layout) and feed dP.
-template <int D, bool CAUSAL, bool BL>
+// workgroup's V rows stay in LDS (natural layout) and feed dP.  DS also
+// writes dS into the panels for the dQ product (zeros for the pairs of
+// a step that a wave skips as wholly masked, which that product reads).
+template <int D, bool CAUSAL, bool BL, bool DS>
 __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   constexpr int QB = RA_DKDV_BN, NMB = QB / 32;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, QB>::ALLOC;
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     dma.load(Qs + buf * TILE, qh, r0, p.N);
     dma.load(Ds + buf * TILE, doh, r0, p.N);
     if (dma.wave < NMB)
-      lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane, rsl + buf * 2 * QB + dma.wave * 64);
+      lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane_here(), rsl + buf * 2 * QB + dma.wave * 64);
   };
   if (n_it > 0) load_rows(walk.cur, 0);
   wait_lds_copies();
@@ -543,15 +552,46 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     n_masked = (CAUSAL && n_it > 0 && blist[0] == t) ? min(n_it, SPB) : 0;
   else
     n_masked = (CAUSAL && qs0 <= k0 + BM - 2) ? min(n_it, (k0 + BM - 2 - qs0) / QB + 1) : 0;
+  // dS panels: a scalar base per step (the block of this wave's 32 keys and
+  // the step's 32 queries) plus this lane's byte offset in it (its key's
+  // 16-query rows, 8 g columns; chunk t adds a 1 KiB half).  A step's dS is
+  // stored at the start of the next step (non-temporal: the dQ pass reads
+  // it once), so the stores have a whole step to complete before the step's
+  // closing wait, which covers them too.
+  const char* const ds_head =
+      DS ? reinterpret_cast<const char*>(p.dsp + (size_t)bh * panel_head(p.N, CAUSAL)) : nullptr;
+  const uint32_t ds_lane = 2u * (16u * l32 + 8u * g);
+  const bool key_ok = key < p.N;
+  half8 ds_pend[2 * NMB];
+  const char* ds_base = nullptr;   // the pending step's row base (uniform), or null
+  auto flush_ds = [&]() {
+    if constexpr (DS) {
+      if (ds_base) {
+#pragma unroll
+        for (int t = 0; t < 2 * NMB; ++t)
+          __builtin_nontemporal_store(
+              ds_pend[t], reinterpret_cast<half8*>(const_cast<char*>(ds_base) + ds_lane + 1024 * t));
+      }
+    }
+  };
   auto step = [&](int it, auto masked) {
     const int r0 = walk.cur;
     const int cur = it & 1;
     if (it + 1 < n_it) load_rows(walk.next, cur ^ 1);
     walk.prefetch(it);
+    flush_ds();
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
-    if (!(CAUSAL && wkey0 > r0 + QB - 1))  // skip tiles wholly before this wave's keys
-      dkdv_tile<D, NMB, decltype(masked)::value>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
-                                                 rsl + cur * 2 * QB, kf, vrow, r0, key, lane);
+    if constexpr (DS)
+      ds_base = ds_head + 2 * (panel_off(r0 / PANEL, p.N, CAUSAL) + (size_t)wkey0 * PANEL +
+                               (size_t)(r0 % PANEL) * 32);
+    if (!(CAUSAL && wkey0 > r0 + QB - 1)) {  // skip tiles wholly before this wave's keys
+      dkdv_tile<D, NMB, decltype(masked)::value, DS>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
+                                                     rsl + cur * 2 * QB, kf, vrow, r0, key, lane,
+                                                     ds_pend, key_ok);
+    } else if constexpr (DS) {
+#pragma unroll
+      for (int t = 0; t < 2 * NMB; ++t) ds_pend[t] = half8{};
+    }
     wait_lds_copies();
     __syncthreads();
     walk.advance(it);
@@ -559,6 +599,7 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   int it = 0;
   for (; it < n_masked; ++it) step(it, std::true_type{});
   for (; it < n_it; ++it) step(it, std::false_type{});
+  flush_ds();
 
   float wv[D / 4];
 #pragma unroll
@@ -588,25 +629,158 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
 }
 
+// ------------------------------------------------------------------ dQ from the dS panels
+// B fragment (8 keys of one query per lane, as the score registers give it)
+// from a 32-key panel tile in LDS, query block c (32 queries), k step ts:
+// in each 16-lane group the 16 lanes point at 4 keys x 16 queries of the
+// block's half b (4 consecutive queries each, 128 contiguous bytes: no bank
+// conflict) and the transposing read hands lane j query j's 4 keys.
+__device__ __forceinline__ half8 panel_frag(const half_t* tile, int c, int ts, int lane) {
+  const int s16 = lane & 15, b = (lane >> 4) & 1, g = lane >> 5;
+  const half_t* p = tile + c * 1024 + b * 512 + (16 * ts + 8 * g + (s16 >> 2)) * 16 + 4 * (s16 & 3);
+  const s16x4 lo = ds_read_tr(p), hi = ds_read_tr(p + 4 * 16);
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(half8, both);
+}
+
+// dQ~ = dS K~ over the panels the dK/dV pass wrote: a plain product, no
+// score recomputation.  Workgroup = the PANEL (256) query rows of one panel,
+// 4 waves x 64 rows; streams 32-key tiles of the panel (16 KiB, contiguous,
+// copied as is) and of K~ through a ring of DQP_STAGES LDS buffers, so that
+// DQP_STAGES - 1 tiles are in flight while one is computed (the panel is
+// read once from HBM, and the copies in flight cover its latency; it is
+// streamed with the non-temporal hint).  Both operands are read transposed:
+// the panel gives the B fragments (8 keys of one query per lane), K~
+// columns the A fragments, and each K~ fragment feeds the wave's two 32-row
+// blocks.  Pairs after a query's diagonal hold zeros in the panel; a wave
+// skips tiles wholly after its rows.  Waves whose rows lie in the exact
+// corner only help load.
+constexpr int DQP_KB = 32;
+constexpr int DQP_TS = DQP_KB * PANEL;   // halfs per panel tile (16 KiB)
+#ifndef RA_DQP_STAGES
+#define RA_DQP_STAGES 3
+#endif
+constexpr int DQP_STAGES = RA_DQP_STAGES;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) {
+  constexpr int CB = D / 32, TK = TileDMA<D, DQP_KB>::ALLOC, TS = DQP_TS;
+  constexpr int NS = DQP_STAGES;
+  static_assert(TS * 2 == 16 * 1024, "four 1 KiB copies per wave per panel tile");
+  __shared__ __attribute__((aligned(16))) half_t Ks[NS * TK];
+  __shared__ __attribute__((aligned(16))) half_t Ss[NS * TS];
+  __shared__ float red[4 * (D / 2)];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int BH = p.B * p.H;
+  const int np = n_panels(p.N), t0 = p.corner / PANEL;
+  int bh, t;
+  map_block(blockIdx.x, BH, np - t0, true, bh, t);
+  const int slot = p.slot0 + blockIdx.x;
+  t += t0;
+  const int q0 = t * PANEL, wrow0 = q0 + 64 * w;
+  const size_t head = (size_t)bh * p.N * D;
+  const half_t* kh = p.kh + head;
+  const half_t* panel = p.dsp + (size_t)bh * panel_head(p.N, CAUSAL) + panel_off(t, p.N, CAUSAL);
+  const bool active = wrow0 + 64 > p.corner && wrow0 < p.N;
+  // keys of this panel below N, in whole tiles (the panel rows are a
+  // multiple of the tile; a ragged last tile holds zeros past N)
+  const int nkeys = min(panel_rows(t, p.N, CAUSAL), (p.N + DQP_KB - 1) / DQP_KB * DQP_KB);
+  const int n_kt = nkeys / DQP_KB;
+
+  f32x16 acc[2][CB];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[j][cb] = f32x16{};
+  }
+  TileDMA<D, DQP_KB> dmk;
+  dmk.init(lane, w);
+  const int wave = __builtin_amdgcn_readfirstlane(w);
+  // copies this wave issues per tile (uniform); every outstanding vector
+  // memory operation of the loop is such a copy
+  const int per_tile = dmk.count() + 4;
+  auto load = [&](int kt) {
+    const int b = kt % NS;
+    dmk.load(Ks + b * TK, kh, kt * DQP_KB, p.N);
+    // the panel tile: 1 KiB blocks wave + 4 i, lane l at byte 16 l
+    const uint32_t tb = (uint32_t)kt * (uint32_t)(2 * DQP_TS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_copy16_nt(panel, tb + 1024u * (wave + 4 * i) + 16u * lane, Ss + b * TS + (wave + 4 * i) * 512);
+  };
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) {
+    if (i < n_kt) load(i);
+  }
+  // tile 0 landed: at most the later prologue tiles outstanding
+  wait_vm(per_tile * max(0, min(NS - 1, n_kt) - 1));
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * DQP_KB;
+    const int ck = (kt % NS) * TK, cs = (kt % NS) * TS;
+    // into the buffer every wave finished reading before the last barrier
+    if (kt + NS - 1 < n_kt) load(kt + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next tiles' copies ahead of the compute
+    if (active && !(CAUSAL && k0 > wrow0 + 63)) {
+#pragma unroll
+      for (int ts = 0; ts < DQP_KB / 16; ++ts) {
+        const half8 b0 = panel_frag(Ss + cs, 2 * w, ts, lane);
+        const half8 b1 = panel_frag(Ss + cs, 2 * w + 1, ts, lane);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const half8 a = tr_frag<D>(Ks + ck, ts, cb, lane);
+          acc[0][cb] = mfma(a, b0, acc[0][cb]);
+          acc[1][cb] = mfma(a, b1, acc[1][cb]);
+        }
+      }
+    }
+    // tile kt + 1 landed: the tiles after it may stay in flight
+    wait_vm(per_tile * max(0, min(NS - 2, n_kt - kt - 2)));
+    __syncthreads();
+  }
+
+  float wv[D / 4], wj[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qrow = wrow0 + 32 * j + l32;
+    if (active && qrow >= p.corner && qrow < p.N) {
+      finish_rows<D>(acc[j], p.scale, nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
+                     head + (size_t)qrow * D, p.bf16, p.dq + head + (size_t)qrow * D, (float)qrow,
+                     wj, g);
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) wv[i] += wj[i];
+    }
+  }
+  store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
+}
+
 int fwd_blocks(const MfmaParams& p) {  // dQ workgroups: 128-row tiles past the corner
   const int tiles = (p.N + BM - 1) / BM - p.corner / BM;
   return tiles > 0 ? p.B * p.H * tiles : 0;
 }
 int dkdv_blocks(const MfmaParams& p) { return p.B * p.H * ((p.N + BM - 1) / BM); }
+int dq_panel_blocks(const MfmaParams& p) {  // panels past the corner
+  const int np = n_panels(p.N) - p.corner / PANEL;
+  return np > 0 ? p.B * p.H * np : 0;
+}
 
 }  // namespace
 
-int dq_mfma_slots(const MfmaParams& p) { return fwd_blocks(p); }
+int dq_mfma_slots(const MfmaParams& p) { return p.dsp ? dq_panel_blocks(p) : fwd_blocks(p); }
 int dkdv_mfma_slots(const MfmaParams& p) { return dkdv_blocks(p); }
 
-#define RA_LAUNCH1(KERNEL, BL)                                                                  \
+#define RA_LAUNCH1(KERNEL, ...)                                                                 \
   do {                                                                                         \
     if (p.D == 64) {                                                                           \
-      if (p.causal) hipLaunchKernelGGL((KERNEL<64, true, BL>), grid, block, 0, s, p);          \
-      else hipLaunchKernelGGL((KERNEL<64, false, BL>), grid, block, 0, s, p);                  \
+      if (p.causal) hipLaunchKernelGGL((KERNEL<64, true, ##__VA_ARGS__>), grid, block, 0, s, p); \
+      else hipLaunchKernelGGL((KERNEL<64, false, ##__VA_ARGS__>), grid, block, 0, s, p);       \
     } else {                                                                                   \
-      if (p.causal) hipLaunchKernelGGL((KERNEL<128, true, BL>), grid, block, 0, s, p);         \
-      else hipLaunchKernelGGL((KERNEL<128, false, BL>), grid, block, 0, s, p);                 \
+      if (p.causal) hipLaunchKernelGGL((KERNEL<128, true, ##__VA_ARGS__>), grid, block, 0, s, p); \
+      else hipLaunchKernelGGL((KERNEL<128, false, ##__VA_ARGS__>), grid, block, 0, s, p);      \
     }                                                                                          \
   } while (0)
 #define RA_LAUNCH(KERNEL, BLOCKS)                                                               \
@@ -621,12 +795,22 @@ void launch_fwd_mfma(const MfmaParams& p, hipStream_t s) {
   if (nb > 0) RA_LAUNCH(fwd_kernel, nb);
 }
 void launch_dq_mfma(const MfmaParams& p, hipStream_t s) {
+  if (p.dsp) {  // dense attention with the dS panels written by the dK/dV pass
+    const int nb = dq_panel_blocks(p);
+    const dim3 grid((unsigned)nb), block(256);
+    if (nb > 0) RA_LAUNCH1(dq_panel_kernel);
+    return;
+  }
   const int nb = fwd_blocks(p);
   if (nb > 0) RA_LAUNCH(dq_kernel, nb);
 }
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s) {
   const int nb = dkdv_blocks(p);
-  if (nb > 0) RA_LAUNCH(dkdv_kernel, nb);
+  if (nb <= 0) return;
+  const dim3 grid((unsigned)nb), block(256);
+  if (p.bmask) RA_LAUNCH1(dkdv_kernel, true, false);
+  else if (p.dsp) RA_LAUNCH1(dkdv_kernel, false, true);
+  else RA_LAUNCH1(dkdv_kernel, false, false);
 }
 
 }  // namespace ra

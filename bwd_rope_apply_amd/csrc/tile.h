@@ -121,6 +121,18 @@ __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, con
       : "v"(voff), "s"(gbase), "s"(m0v)
       : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for data read once (streamed
+// past the caches rather than kept in them).
+__device__ __forceinline__ void lds_copy16_nt(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
+      : "v"(voff), "s"(gbase), "s"(m0v)
+      : "memory", "m0");
+}
 __device__ __forceinline__ void lds_copy4(const void* gbase, uint32_t voff, const void* lds) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
   asm volatile(
@@ -153,16 +165,22 @@ struct TileDMA {
   }
   // block wave + 4 i exists for every wave in the full rounds i < NBLK / 4
   __device__ __forceinline__ bool issued(int i) const { return i < NBLK / 4 || wave + 4 * i < NBLK; }
+  // copy instructions this wave issues per load (uniform)
+  __device__ __forceinline__ int count() const { return NBLK / 4 + (wave < NBLK % 4 ? 1 : 0); }
   // src is the head's plane; byte offsets within a plane fit 32 bits
   // (N D 2 <= 2^32 for every accepted shape), so the address is a scalar
   // base plus one zero-extended 32-bit lane offset: the scalar-base form
+  template <bool NT = false>
   __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0, int N) const {
     const char* base = reinterpret_cast<const char*>(src);
     const uint32_t rb = (uint32_t)r0 * (uint32_t)(2 * D);
     if (r0 + ROWS <= N) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        if (issued(i)) lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
+        if (issued(i)) {
+          if constexpr (NT) lds_copy16_nt(base, rb + off[i], tile + (wave + 4 * i) * 512);
+          else lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
+        }
       }
     } else {
 #pragma unroll
@@ -255,6 +273,45 @@ __device__ __forceinline__ int column_blocks(const uint32_t* bm, int nb, int W, 
 }
 
 __device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wait until at most n (uniform, 0..15) vector memory operations of this
+// wave are outstanding, ignoring the other counters.  Only for a wave whose
+// outstanding vector memory operations are all loads: those complete in
+// issue order, so the oldest n' - n have landed.
+template <int N>
+__device__ __forceinline__ void wait_vm_const() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: wait_vm_const<0>(); break;
+    case 1: wait_vm_const<1>(); break;
+    case 2: wait_vm_const<2>(); break;
+    case 3: wait_vm_const<3>(); break;
+    case 4: wait_vm_const<4>(); break;
+    case 5: wait_vm_const<5>(); break;
+    case 6: wait_vm_const<6>(); break;
+    case 7: wait_vm_const<7>(); break;
+    case 8: wait_vm_const<8>(); break;
+    case 9: wait_vm_const<9>(); break;
+    case 10: wait_vm_const<10>(); break;
+    case 11: wait_vm_const<11>(); break;
+    case 12: wait_vm_const<12>(); break;
+    case 13: wait_vm_const<13>(); break;
+    case 14: wait_vm_const<14>(); break;
+    default: wait_vm_const<0>(); break;   // n >= 15: wait for all (conservative)
+  }
+}
+
+// The lane index, computed where it is used (two VALU instructions that the
+// compiler cannot hoist): under register pressure this is cheaper than
+// keeping it live across a loop, which the compiler may do by spilling it.
+__device__ __forceinline__ uint32_t lane_here() {
+  uint32_t x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
 
 template <int D>
 __device__ __forceinline__ void load_frag_rows(half8* f, const half_t* src, int row, int N, int g) {

@@ -73,7 +73,7 @@ typedef enum {
   ROPE_ATTN_ERR_SHAPE = -2,     /* B, H, N < 1, D not 64 or 128, or sizes overflow */
   ROPE_ATTN_ERR_DTYPE = -3,     /* dtype not a rope_attn_dtype */
   ROPE_ATTN_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
-  ROPE_ATTN_ERR_WORKSPACE = -5, /* workspace smaller than the *_workspace_bytes query */
+  ROPE_ATTN_ERR_WORKSPACE = -5, /* workspace smaller than the *_workspace_bytes(_min) query */
   ROPE_ATTN_ERR_HIP = -6,       /* the HIP runtime reported a launch error */
   ROPE_ATTN_ERR_ARG = -7        /* base not finite and > 0, or causal not 0/1 */
 } rope_attn_status;
@@ -90,8 +90,21 @@ int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* 
                   int N, int D, int dtype, double base, const float* alpha, int causal,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by rope_attn_bwd; 0 on invalid arguments. */
+/* Workspace for rope_attn_bwd; 0 on invalid arguments.  With bf16 inputs it
+ * includes the dS panels: the dK/dV pass stores dS = P o (dP - D_i) in fp16
+ * there (about B*H*N^2 bytes under the causal mask, 2*B*H*N^2 without it)
+ * and dQ is then one product dS K~ instead of a pass that recomputes the
+ * scores and dP.  The panels are included when they take at most 16 GiB;
+ * block-list calls do not use them.  A workspace of at least
+ * rope_attn_bwd_workspace_bytes_min but smaller than this selects the
+ * recomputing dQ pass; the two agree within the bf16 tolerance (the same dS
+ * values, summed in another order). */
 size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal);
+
+/* The smallest workspace rope_attn_bwd accepts (no dS panels); equal to
+ * rope_attn_bwd_workspace_bytes for fp32 inputs and when the panels would
+ * exceed 16 GiB; 0 on invalid arguments. */
+size_t rope_attn_bwd_workspace_bytes_min(int B, int H, int N, int D, int dtype, int causal);
 
 /* Backward.  q, k, v, dO: [B,H,N,D] of `dtype`; o, lse: the forward's float32
  * outputs for the same q, k, v, base, alpha, causal.  dq, dk, dv: [B,H,N,D]
@@ -112,8 +125,10 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
  *   EXACT   the float32 path: whole problem (fp32 inputs) or the leading
  *           causal corner, query rows < 128 (bf16 inputs)
  *   MAIN    forward matrix-core pass (bf16 inputs)
- *   DQ      dQ matrix-core pass (bf16 inputs)
- *   DKDV    dK, dV matrix-core pass (bf16 inputs)
+ *   DKDV    dK, dV matrix-core pass (bf16 inputs); with the dS panels it
+ *           also writes dS into the workspace
+ *   DQ      dQ matrix-core pass (bf16 inputs); with the dS panels it reads
+ *           the dS that DKDV left, so DKDV must have run first
  *   DALPHA  fixed-order reduction of the d alpha partials
  *   PREP_GRAD  (backward only, in place of PREP) the dO plane and D_i only:
  *           the frequency table and the Q~, K~, V planes are taken from the
@@ -129,8 +144,8 @@ typedef enum {
   ROPE_ATTN_STAGE_PREP = 1,
   ROPE_ATTN_STAGE_EXACT = 2,
   ROPE_ATTN_STAGE_MAIN = 4,
-  ROPE_ATTN_STAGE_DQ = 8,
-  ROPE_ATTN_STAGE_DKDV = 16,
+  ROPE_ATTN_STAGE_DKDV = 8,
+  ROPE_ATTN_STAGE_DQ = 16,
   ROPE_ATTN_STAGE_DALPHA = 32,
   ROPE_ATTN_STAGE_ALL = 63,
   ROPE_ATTN_STAGE_PREP_GRAD = 64

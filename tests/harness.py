@@ -25,18 +25,25 @@ def device_opts(opts, device="cuda"):
     return d
 
 
-def run_gpu(inp: W.Inputs, causal=None, alpha=True, want_dalpha=True, opts=None):
+def run_gpu(inp: W.Inputs, causal=None, alpha=True, want_dalpha=True, opts=None, ws="bwd"):
     """Forward and backward on the GPU; returns float64 numpy arrays.  opts:
-    a dict of options (unrotated_pairs, scale, pos_offset, block_lists)."""
+    a dict of options (unrotated_pairs, scale, pos_offset, block_lists).
+    ws: the backward workspace size query, "bwd" (with the dS panels where
+    they apply) or "bwd_min" (dQ recomputes the scores)."""
     import torch
-    from bwd_rope_apply_amd import fwd, bwd
+    from bwd_rope_apply_amd import fwd, bwd, _lib
     wl = inp.wl
     causal = wl.causal if causal is None else causal
     q, k, v, do = (to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
     a = to_device(inp.alpha) if alpha else None
     opts = device_opts(opts)
     o, lse = fwd(q, k, v, wl.base, a, causal, opts=opts)
-    dq, dk, dv, da = bwd(q, k, v, o, do, lse, wl.base, a, causal, want_dalpha=want_dalpha, opts=opts)
+    B, H, N, D = q.shape
+    dt = _lib.BF16 if wl.dtype == "bf16" else _lib.FP32
+    work = torch.empty(max(1, _lib.workspace_bytes(ws, B, H, N, D, dt, causal)), dtype=torch.uint8,
+                       device="cuda")
+    dq, dk, dv, da = bwd(q, k, v, o, do, lse, wl.base, a, causal, workspace=work,
+                         want_dalpha=want_dalpha, opts=opts)
     torch.cuda.synchronize()
     out = dict(O=o, LSE=lse, dQ=dq, dK=dk, dV=dv, dalpha=da)
     return {n: (None if t is None else t.double().cpu().numpy()) for n, t in out.items()}

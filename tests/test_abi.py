@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == ["gram_cascade", "gram_cascade_workspace_bytes", "gram_select",
                            "gram_select_stages", "gram_select_workspace_bytes",
                            "rope_attn_bwd", "rope_attn_bwd_ex", "rope_attn_bwd_stages",
-                           "rope_attn_bwd_workspace_bytes", "rope_attn_fwd", "rope_attn_fwd_ex",
+                           "rope_attn_bwd_workspace_bytes", "rope_attn_bwd_workspace_bytes_min",
+                           "rope_attn_fwd", "rope_attn_fwd_ex",
                            "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
                            "rope_attn_status_string"]
 
@@ -119,6 +120,32 @@ def test_block_list_validation(lib, N, ptr, idx, nnz, status):
     assert lib.rope_attn_fwd_ex(63, ctypes.addressof(op), *args) == status
     bargs = [A] * 10 + [1, 1, N, 64, 1, 1e4, None, 1, A, 1 << 40, None]
     assert lib.rope_attn_bwd_ex(63, ctypes.addressof(op), *bargs) == status
+
+
+def _panel_bytes(B, H, N, causal):
+    """fp16 dS panels: one per 256-query block, [keys][256]; under the causal
+    mask panel b keeps keys 0 .. 256 (b + 1) - 1."""
+    n = -(-N // 256)
+    per_head = 256 * 256 * n * (n + 1) // 2 if causal else n * 256 * 256 * n
+    return 2 * B * H * per_head
+
+
+def test_workspace_panels(lib):
+    """The full backward workspace adds the dS panels (bf16, up to 16 GiB),
+    at the end of the layout; the minimal one is the recomputing layout."""
+    for B, H, N, causal in ((1, 32, 8192, 1), (2, 3, 1000, 0), (1, 1, 1, 1), (1, 8, 32768, 1)):
+        full = lib.rope_attn_bwd_workspace_bytes(B, H, N, 128, 1, causal)
+        lo = lib.rope_attn_bwd_workspace_bytes_min(B, H, N, 128, 1, causal)
+        pb = _panel_bytes(B, H, N, causal)
+        assert full - lo == (pb + 255) // 256 * 256, (B, H, N, causal)
+        assert lo > lib.rope_attn_fwd_workspace_bytes(B, H, N, 128, 1, causal)
+    # fp32 inputs never use panels; above 16 GiB of panels neither does bf16
+    assert (lib.rope_attn_bwd_workspace_bytes(1, 4, 4096, 64, 0, 1)
+            == lib.rope_attn_bwd_workspace_bytes_min(1, 4, 4096, 64, 0, 1))
+    assert _panel_bytes(1, 64, 32768, 1) > 16 << 30
+    assert (lib.rope_attn_bwd_workspace_bytes(1, 64, 32768, 64, 1, 1)
+            == lib.rope_attn_bwd_workspace_bytes_min(1, 64, 32768, 64, 1, 1))
+    assert lib.rope_attn_bwd_workspace_bytes_min(1, 1, 16, 96, 1, 1) == 0   # bad D
 
 
 def test_workspace_covers_block_lists(lib):

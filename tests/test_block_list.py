@@ -57,18 +57,19 @@ def test_bf16_diagonal_only(causal):
 @pytest.mark.parametrize("N,causal", [(700, True), (832, True), (700, False), (832, False)])
 def test_full_lists_match_dense(N, causal):
     """Lists naming every block give dense attention.  Under the causal mask
-    the kernels walk the same tiles in the same order as the dense path
-    (the exact corner is one block in both at N <= 8192), so the results are
-    bit-identical; without it the ragged block may take the masked tile body
-    where the dense path does not, which changes no value but is compared to
-    1e-6 of the RMS."""
+    the kernels walk the same tiles in the same order as the dense path that
+    recomputes the scores for dQ (the smallest workspace; block lists never
+    use the dS panels), and the exact corner is one block in both at
+    N <= 8192, so the results are bit-identical; without it the ragged block
+    may take the masked tile body where the dense path does not, which
+    changes no value but is compared to 1e-6 of the RMS."""
     import torch
     wl = W.get("layer_2k", B=1, H=2, N=N, seed=N)
     inp = W.make_inputs(wl)
     nb = (N + 127) // 128
     full = [[[list(range(nb))] * nb for _ in range(wl.H)] for _ in range(wl.B)]
     print(wl.name, causal, flush=True)
-    a = Hn.run_gpu(inp, causal)
+    a = Hn.run_gpu(inp, causal, ws="bwd_min")
     b = Hn.run_gpu(inp, causal, opts=dict(block_lists=full))
     for n in NAMES + ("LSE",):
         d = float(np.max(np.abs(a[n] - b[n])))

@@ -6,6 +6,8 @@ max |err| / rms(ref) <= 2e-2 per tensor (O, dQ, dK, dV, dalpha) and LSE
 within 2e-2 absolute.  Sizes span several 128-row tiles, a ragged tail,
 the exact corner and the degenerate N = 1.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -19,8 +21,8 @@ BF16_TOL = 2e-2
 NAMES = ("O", "dQ", "dK", "dV", "dalpha")
 
 
-def _check(inp, causal=None, alpha=True, opts=None):
-    got = Hn.run_gpu(inp, causal, alpha, opts=opts)
+def _check(inp, causal=None, alpha=True, opts=None, ws="bwd"):
+    got = Hn.run_gpu(inp, causal, alpha, opts=opts, ws=ws)
     ref = Hn.run_oracle(inp, causal, alpha, opts=opts)
     for n in NAMES + ("LSE",):
         assert np.isfinite(got[n]).all(), n
@@ -77,6 +79,59 @@ def test_bf16_noncausal(D):
     wl = W.Workload("bf16_full", 1, 2, 333, D, "bf16", 1e4, False, ("normal", 1.0, 1.0),
                     ("normal", 1.0, 1.0), ("normal", 1.0, 1.0), ("normal", 0.2, 1.0), seed=91)
     _check(W.make_inputs(wl), causal=False)
+
+
+# The backward with the smallest workspace: no dS panels, so dQ recomputes
+# the scores and dP instead of reading the dS that the dK/dV pass stored.
+RECOMPUTE_CASES = [("long_8k", 3, 700, True), ("layer_2k", 2, 129, True), ("layer_2k", 2, 1, True),
+                   ("vlong_32k", 2, 700, True), ("layer_2k", 1, 333, False),
+                   ("vlong_32k", 1, 333, False)]
+
+
+@pytest.mark.parametrize("name,H,N,causal", RECOMPUTE_CASES)
+def test_bf16_recomputing_dq(name, H, N, causal):
+    wl = dataclasses.replace(W.get(name, B=1, H=H, N=N), causal=causal)
+    _check(W.make_inputs(wl), causal=causal, ws="bwd_min")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_panels_and_recomputation_agree(causal):
+    """The two dQ passes on the same inputs: dK and dV come from the same
+    dK/dV kernel arithmetic (bit-identical); dQ and dalpha sum the same dS
+    values in another order, so they agree to well within the bar."""
+    wl = W.get("long_8k", B=1, H=2, N=900)
+    inp = W.make_inputs(wl)
+    a = Hn.run_gpu(inp, causal=causal)
+    b = Hn.run_gpu(inp, causal=causal, ws="bwd_min")
+    for n in ("O", "LSE", "dK", "dV"):
+        assert np.array_equal(a[n], b[n]), n
+    for n in ("dQ", "dalpha"):
+        e = Hn.err_rms(a[n], b[n])
+        print(n, e)
+        assert e <= 2e-3, (n, e)
+
+
+def test_staged_backward_in_stage_order():
+    """Every backward stage in its own call, in increasing bit order (DKDV
+    before DQ, which reads the panels DKDV wrote), is bit-identical to the
+    one-call backward."""
+    import torch
+    from bwd_rope_apply_amd import _lib, fwd, bwd
+    wl = W.get("long_8k", B=1, H=2, N=777)
+    inp = W.make_inputs(wl)
+    q, k, v, do = (Hn.to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    a = Hn.to_device(inp.alpha)
+    ws = torch.empty(_lib.workspace_bytes("bwd", 1, 2, 777, 128, _lib.BF16, True), dtype=torch.uint8,
+                     device="cuda")
+    o, lse = fwd(q, k, v, wl.base, a, True, workspace=ws)
+    ref = [t.clone() for t in bwd(q, k, v, o, do, lse, wl.base, a, True, workspace=ws)]
+    outs = tuple(torch.full_like(t, float("nan")) for t in ref)
+    for bit in (_lib.STAGE_PREP, _lib.STAGE_EXACT, _lib.STAGE_MAIN, _lib.STAGE_DKDV, _lib.STAGE_DQ,
+                _lib.STAGE_DALPHA):
+        bwd(q, k, v, o, do, lse, wl.base, a, True, workspace=ws, out=outs, stages=bit)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, outs):
+        assert torch.equal(x, y)
 
 
 def test_bf16_standard_rope_alpha_null():
