@@ -34,9 +34,42 @@ void launch_table(const TableParams& p, hipStream_t s) {
 // (pairs (2m, 2m+1) turned by +p theta_hat_m), V and dO converted; every
 // output plane is fp16.  D_i = sum_c dO_ic O_ic is the gamma_2 row scalar of
 // "RoPE attention can be trained in almost-linear time" (Methodology 2).
-__device__ __forceinline__ void load8(const void* base, size_t idx, int bf16, float* x) {
-  load4(base, idx, bf16, x);
-  load4(base, idx + 4, bf16, x + 4);
+// The pass is bound by HBM: every input of a thread is loaded (one 16-byte
+// load per bf16 chunk) before anything is stored, so all its loads are in
+// flight together.
+// 8 consecutive input elements as stored (bf16: one uint4; fp32: two), and
+// their float values; loading and converting are separate steps so that a
+// thread's loads are all issued before the first conversion waits
+struct Raw8 {
+  uint4 a, b;
+};
+template <bool BF16>
+__device__ __forceinline__ Raw8 load8(const void* base, size_t idx) {
+  Raw8 r;
+  if constexpr (BF16) {
+    r.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    r.b = r.a;
+  } else {
+    const uint4* f = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + idx);
+    r.a = f[0];
+    r.b = f[1];
+  }
+  return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8& r, float* x) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
+  }
 }
 
 __device__ __forceinline__ void store8h(half_t* dst, const float* x) {
@@ -54,6 +87,9 @@ __device__ __forceinline__ void store8lo(half_t* dst, const float* x) {
   *reinterpret_cast<half8*>(dst) = h;
 }
 
+// BF16: the input storage (compile time, so that no branch separates a
+// load from its use and every load of a thread issues before the first wait)
+template <bool BF16>
 __global__ void prep_kernel(PrepParams p) {
   const int cpr = p.D / 8;                        // chunks per row (8 or 16)
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -63,43 +99,55 @@ __global__ void prep_kernel(PrepParams p) {
   const int chunk = (int)(gid % cpr);
   const int pos = (int)(row % p.N);
   const size_t e0 = (size_t)row * p.D + (size_t)chunk * 8;
-  float x[8];
+  float xq[8], xk[8], xv[8], xd[8];
+  Raw8 rq = {}, rk = {}, rv = {}, rd = {};
+  float4 oa = {}, ob = {};
+  float2 cs[4] = {};
   if (live) {
-    const float2* cs = p.cs + (size_t)pos * (p.D / 2) + chunk * 4;
-    if (p.qh) {
-      load8(p.q, e0, p.bf16, x);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rot(cs[i].x, cs[i].y, x[2 * i], x[2 * i + 1]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] *= p.qscale;
-      store8h(p.qh + e0, x);
-      if (p.qlo && pos < p.rlo)
-        store8lo(p.qlo + ((size_t)(row / p.N) * p.rlo + pos) * p.D + chunk * 8, x);
+    if (p.qh) rq = load8<BF16>(p.q, e0);
+    if (p.kh) rk = load8<BF16>(p.k, e0);
+    if (p.vh) rv = load8<BF16>(p.v, e0);
+    if (p.doh || p.drow) rd = load8<BF16>(p.dO, e0);
+    if (p.drow) {
+      const float4* o4 = reinterpret_cast<const float4*>(p.o + e0);
+      oa = o4[0];
+      ob = o4[1];
     }
-    if (p.kh) {
-      load8(p.k, e0, p.bf16, x);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rot(cs[i].x, cs[i].y, x[2 * i], x[2 * i + 1]);
-      store8h(p.kh + e0, x);
-      if (p.klo && pos < p.rlo)
-        store8lo(p.klo + ((size_t)(row / p.N) * p.rlo + pos) * p.D + chunk * 8, x);
+    if (p.qh || p.kh) {
+      const float4* c4 = reinterpret_cast<const float4*>(p.cs + (size_t)pos * (p.D / 2) + chunk * 4);
+      const float4 c01 = c4[0], c23 = c4[1];
+      cs[0] = make_float2(c01.x, c01.y); cs[1] = make_float2(c01.z, c01.w);
+      cs[2] = make_float2(c23.x, c23.y); cs[3] = make_float2(c23.z, c23.w);
     }
-    if (p.vh) {
-      load8(p.v, e0, p.bf16, x);
-      store8h(p.vh + e0, x);
+    unpack8<BF16>(rq, xq);
+    unpack8<BF16>(rk, xk);
+    unpack8<BF16>(rv, xv);
+    unpack8<BF16>(rd, xd);
+    // all arithmetic before the first store: a wait for a load issued
+    // before a store also waits for that store
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rot(cs[i].x, cs[i].y, xq[2 * i], xq[2 * i + 1]);
+      rot(cs[i].x, cs[i].y, xk[2 * i], xk[2 * i + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xq[i] *= p.qscale;
+    if (p.qh) store8h(p.qh + e0, xq);
+    if (p.kh) store8h(p.kh + e0, xk);
+    if (p.vh) store8h(p.vh + e0, xv);
+    if (pos < p.rlo) {
+      const size_t lo = ((size_t)(row / p.N) * p.rlo + pos) * p.D + chunk * 8;
+      if (p.qh && p.qlo) store8lo(p.qlo + lo, xq);
+      if (p.kh && p.klo) store8lo(p.klo + lo, xk);
     }
   }
   if (p.doh || p.drow) {
     float acc = 0.f;
     if (live) {
-      load8(p.dO, e0, p.bf16, x);
-      if (p.doh) store8h(p.doh + e0, x);
-      if (p.drow) {
-        const float4* o4 = reinterpret_cast<const float4*>(p.o + e0);
-        float4 a = o4[0], b = o4[1];
-        acc = x[0] * a.x + x[1] * a.y + x[2] * a.z + x[3] * a.w +
-              x[4] * b.x + x[5] * b.y + x[6] * b.z + x[7] * b.w;
-      }
+      if (p.doh) store8h(p.doh + e0, xd);
+      if (p.drow)
+        acc = xd[0] * oa.x + xd[1] * oa.y + xd[2] * oa.z + xd[3] * oa.w +
+              xd[4] * ob.x + xd[5] * ob.y + xd[6] * ob.z + xd[7] * ob.w;
     }
     if (p.drow) {
       // the cpr lanes of a row are consecutive and aligned inside the wave
@@ -125,7 +173,9 @@ __global__ void prep_kernel(PrepParams p) {
 
 void launch_prep(const PrepParams& p, hipStream_t s) {
   const long total = (long)p.BH * p.N * (p.D / 8);
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (p.bf16) hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(prep_kernel<false>, grid, block, 0, s, p);
 }
 
 // Block visibility rows from a CSR list, one wave per (bh, query block):
