@@ -698,9 +698,19 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   TileDMA<D, DQP_KB> dmk;
   dmk.init(lane, w);
   const int wave = __builtin_amdgcn_readfirstlane(w);
-  // copies this wave issues per tile (uniform); every outstanding vector
-  // memory operation of the loop is such a copy
-  const int per_tile = dmk.count() + 4;
+  // Copies this wave issues per tile: KLO or KLO + 1 for K~, 4 for the panel.
+  // Every outstanding vector memory operation of the loop is such a copy, so
+  // "tile i landed" is "at most (copies per tile) x (tiles issued after i)
+  // outstanding".  In the steady state NS - 2 tiles stay in flight; the last
+  // steps wait for everything.
+  constexpr int KLO = TileDMA<D, DQP_KB>::NBLK / 4;
+  static_assert((KLO + 5) * (NS - 2) < 64, "vmcnt range");
+  const bool khi = dmk.count() > KLO;
+  auto wait_landed = [&](bool steady) {
+    if (!steady) wait_vm_const<0>();
+    else if (khi) wait_vm_const<(KLO + 5) * (NS - 2)>();
+    else wait_vm_const<(KLO + 4) * (NS - 2)>();
+  };
   auto load = [&](int kt) {
     const int b = kt % NS;
     dmk.load(Ks + b * TK, kh, kt * DQP_KB, p.N);
@@ -714,8 +724,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   for (int i = 0; i < NS - 1; ++i) {
     if (i < n_kt) load(i);
   }
-  // tile 0 landed: at most the later prologue tiles outstanding
-  wait_vm(per_tile * max(0, min(NS - 1, n_kt) - 1));
+  wait_landed(n_kt >= NS - 1);   // tile 0
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * DQP_KB;
@@ -736,8 +745,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
         }
       }
     }
-    // tile kt + 1 landed: the tiles after it may stay in flight
-    wait_vm(per_tile * max(0, min(NS - 2, n_kt - kt - 2)));
+    wait_landed(kt + NS - 1 < n_kt);   // tile kt + 1
     __syncthreads();
   }
 

@@ -274,34 +274,14 @@ __device__ __forceinline__ int column_blocks(const uint32_t* bm, int nb, int W, 
 
 __device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Wait until at most n (uniform, 0..15) vector memory operations of this
-// wave are outstanding, ignoring the other counters.  Only for a wave whose
-// outstanding vector memory operations are all loads: those complete in
-// issue order, so the oldest n' - n have landed.
+// Wait until at most N (0..63) vector memory operations of this wave are
+// outstanding, ignoring the other counters.  On gfx9 loads, stores and
+// global -> LDS copies share this counter and retire from it in issue
+// order, so everything older than the N most recent has completed.
 template <int N>
 __device__ __forceinline__ void wait_vm_const() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: wait_vm_const<0>(); break;
-    case 1: wait_vm_const<1>(); break;
-    case 2: wait_vm_const<2>(); break;
-    case 3: wait_vm_const<3>(); break;
-    case 4: wait_vm_const<4>(); break;
-    case 5: wait_vm_const<5>(); break;
-    case 6: wait_vm_const<6>(); break;
-    case 7: wait_vm_const<7>(); break;
-    case 8: wait_vm_const<8>(); break;
-    case 9: wait_vm_const<9>(); break;
-    case 10: wait_vm_const<10>(); break;
-    case 11: wait_vm_const<11>(); break;
-    case 12: wait_vm_const<12>(); break;
-    case 13: wait_vm_const<13>(); break;
-    case 14: wait_vm_const<14>(); break;
-    default: wait_vm_const<0>(); break;   // n >= 15: wait for all (conservative)
-  }
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // The lane index, computed where it is used (two VALU instructions that the
