@@ -380,8 +380,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       launch_simt_dkdv(sp, hs);
     } else if (s.corner()) {
       mp.slot0 = 0;
-      launch_corner_dq(mp, hs);
-      launch_corner_dkdv(mp, hs);  // rotated-frame partials, no d alpha slots
+      launch_corner_bwd(mp, hs);  // dK/dV as rotated-frame partials, no d alpha slots
     }
   }
   // dK/dV first: with panels it writes the dS that the dQ product reads

@@ -170,8 +170,7 @@ void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);
 int dq_mfma_slots(const MfmaParams& p);   // either dQ kernel (p.dsp selects)
 int dkdv_mfma_slots(const MfmaParams& p);
 void launch_corner_fwd(const MfmaParams& p, hipStream_t s);
-void launch_corner_dq(const MfmaParams& p, hipStream_t s);
-void launch_corner_dkdv(const MfmaParams& p, hipStream_t s);
+void launch_corner_bwd(const MfmaParams& p, hipStream_t s);   // dQ rows and dK/dV partials
 int corner_dq_slots(const MfmaParams& p);
 void launch_dalpha_reduce(const DalphaParams& p, hipStream_t s);
 

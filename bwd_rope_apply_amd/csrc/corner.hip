@@ -119,8 +119,9 @@ __global__ __launch_bounds__(256) void corner_fwd_kernel(MfmaParams p) {
 }
 
 // ------------------------------------------------------------------ dQ
+// Workgroup bid of the dQ part (its own d alpha slot).
 template <int D>
-__global__ __launch_bounds__(256) void corner_dq_kernel(MfmaParams p) {
+__device__ __forceinline__ void corner_dq(const MfmaParams& p, int bid) {
   constexpr int DT = D / 16, CB = D / 32, TILE = BN * (D + 8);
   __shared__ __attribute__((aligned(16))) half_t Kh[TILE];
   __shared__ __attribute__((aligned(16))) half_t Kl[TILE];
@@ -128,9 +129,9 @@ __global__ __launch_bounds__(256) void corner_dq_kernel(MfmaParams p) {
   __shared__ float red[4 * (D / 2)];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH, t = blockIdx.x / BH;
+  const int bh = bid % BH, t = bid / BH;
   const int q0 = t * BM, wrow0 = q0 + 32 * w, qrow = wrow0 + l32;
-  const int slot = p.slot0 + blockIdx.x;
+  const int slot = p.slot0 + bid;
   const int nlo = min(p.N, p.corner);
   const size_t head = (size_t)bh * p.N * D, lhead = (size_t)bh * p.corner * D;
   const bool row_ok = qrow < nlo;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(256) void corner_dq_kernel(MfmaParams p) {
 // Keys [0, corner) against query rows [key, corner): rotated-frame partial
 // sums of dK~ (final scale) and dV, completed by the main dK/dV pass.
 template <int D>
-__global__ __launch_bounds__(256) void corner_dkdv_kernel(MfmaParams p) {
+__device__ __forceinline__ void corner_dkdv(const MfmaParams& p, int bid) {
   constexpr int DT = D / 16, CB = D / 32, TILE = BN * (D + 8);
   __shared__ __attribute__((aligned(16))) half_t Qh[TILE];
   __shared__ __attribute__((aligned(16))) half_t Ql[TILE];
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void corner_dkdv_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(16))) float drs[BN];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH, t = blockIdx.x / BH;
+  const int bh = bid % BH, t = bid / BH;
   const int k0 = t * BM, wkey0 = k0 + 32 * w, key = wkey0 + l32;
   const int nlo = min(p.N, p.corner);
   if (k0 >= nlo) return;  // whole workgroup
@@ -269,6 +270,15 @@ __global__ __launch_bounds__(256) void corner_dkdv_kernel(MfmaParams p) {
 
 int corner_blocks(const MfmaParams& p) { return p.B * p.H * ((p.corner + BM - 1) / BM); }
 
+// The two backward parts are independent (dQ rows < corner; dK~, dV partials
+// of keys < corner), and each has few workgroups of latency-bound work, so
+// they share one launch: workgroups [0, ndq) take dQ, the rest dK/dV.
+template <int D>
+__global__ __launch_bounds__(256) void corner_bwd_kernel(MfmaParams p, int ndq) {
+  if ((int)blockIdx.x < ndq) corner_dq<D>(p, blockIdx.x);
+  else corner_dkdv<D>(p, blockIdx.x - ndq);
+}
+
 }  // namespace
 
 int corner_dq_slots(const MfmaParams& p) { return corner_blocks(p); }
@@ -278,15 +288,12 @@ void launch_corner_fwd(const MfmaParams& p, hipStream_t s) {
   if (p.D == 64) hipLaunchKernelGGL(corner_fwd_kernel<64>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(corner_fwd_kernel<128>, grid, block, 0, s, p);
 }
-void launch_corner_dq(const MfmaParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)corner_blocks(p)), block(256);
-  if (p.D == 64) hipLaunchKernelGGL(corner_dq_kernel<64>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(corner_dq_kernel<128>, grid, block, 0, s, p);
-}
-void launch_corner_dkdv(const MfmaParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)corner_blocks(p)), block(256);
-  if (p.D == 64) hipLaunchKernelGGL(corner_dkdv_kernel<64>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(corner_dkdv_kernel<128>, grid, block, 0, s, p);
+void launch_corner_bwd(const MfmaParams& p, hipStream_t s) {
+  const int n = corner_blocks(p);
+  if (n <= 0) return;
+  const dim3 grid((unsigned)(2 * n)), block(256);
+  if (p.D == 64) hipLaunchKernelGGL(corner_bwd_kernel<64>, grid, block, 0, s, p, n);
+  else hipLaunchKernelGGL(corner_bwd_kernel<128>, grid, block, 0, s, p, n);
 }
 
 }  // namespace ra
