@@ -561,7 +561,9 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   const char* const ds_head =
       DS ? reinterpret_cast<const char*>(p.dsp + (size_t)bh * panel_head(p.N, CAUSAL)) : nullptr;
   const uint32_t ds_lane = 2u * (16u * l32 + 8u * g);
-  const bool key_ok = key < p.N;
+  // keys at or past N store zeros; under the causal mask every pair of such
+  // a key is masked (every query is below N), so dS is already 0 there
+  const bool key_ok = CAUSAL || key < p.N;
   half8 ds_pend[2 * NMB];
   const char* ds_base = nullptr;   // the pending step's row base (uniform), or null
   auto flush_ds = [&]() {
