@@ -37,6 +37,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_TFLOPS = 2516.6   # fp16 / bf16 dense matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
 HBM_GBS = 8000.0
+FP32_VECTOR_TFLOPS = 157.3   # vector fp32: 256 CU x 128 FMA lanes x 2 flops x 2.4 GHz
 METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
 
 # Stage bits of the C ABI (rope_attn_stage)
@@ -102,13 +103,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(path: str, stage: str):
+def measured_traffic(path: str, stage: str, workload: str):
     """HBM bytes per launch of `stage` from a counter summary, or None if the
-    summary is missing or was taken on other kernel source."""
+    summary is missing, covers another workload or was taken on other
+    kernel source."""
     if not path or not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch", {}).get(stage)
 
@@ -405,8 +407,22 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
 
     dom, kernel, dom_units = DOMINANT
-    achieved = dom_units * unit / (call_ms[dom] * 1e-3) / 1e12
-    traffic = measured_traffic(args.traffic, dom) if args.retrieved < 0 else None
+    if wl.dtype == "bf16":
+        achieved = dom_units * unit / (call_ms[dom] * 1e-3) / 1e12
+        traffic = measured_traffic(args.traffic, dom, wl.name) if args.retrieved < 0 else None
+        roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
+                    "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                    "traffic": traffic, "avg_ms": round(call_ms[dom], 4)}
+        dq_pass = ("recompute" if args.min_workspace or args.retrieved >= 0
+                   or _lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal)
+                   == _lib.workspace_bytes("bwd_min", B, H, N, D, dt_code, wl.causal) else "ds_panels")
+    else:
+        # fp32 inputs: the exact float32 path runs the whole step on the vector ALUs
+        roofline = {"bound": "alu", "kernel": "simt (whole step, fp32 FMA)", "achieved": round(value, 4),
+                    "peak": FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(value / FP32_VECTOR_TFLOPS, 5), "traffic": None,
+                    "avg_ms": round(ms_step, 4)}
+        dq_pass = "fp32_exact"
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -423,14 +439,9 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
                    "base": wl.base, "storage": wl.dtype, "outputs": "fp32",
                    "options": opts_config,
-                   "dq_pass": ("recompute" if args.min_workspace or args.retrieved >= 0
-                               or _lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal)
-                               == _lib.workspace_bytes("bwd_min", B, H, N, D, dt_code, wl.causal)
-                               else "ds_panels"),
+                   "dq_pass": dq_pass,
                    "flops_per_step": flops, "pct_bf16_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
-                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": traffic, "avg_ms": round(call_ms[dom], 4)},
+        "roofline": roofline,
         "calls_ms": {n: round(t, 4) for n, t in call_ms.items()},
         "stages_ms_serial": {n: round(t, 4) for n, t in stage_ms.items()},
         "events_ms": {"step_median": round(float(np.median(step_ev)), 4),
