@@ -25,9 +25,12 @@ struct Shape {
   int corner() const { return (bf16() && causal) ? (blocks ? BLK : corner_rows(N)) : 0; }
   // block visibility bitmask (any call that may use block lists)
   bool mask_ok() const { return N <= MAX_BLOCKS * BLK; }
-  // dS panels for the backward's dQ product (bf16, up to PANEL_MAX_BYTES)
+  // dS panels for the backward's dQ product (bf16, D = 128, up to
+  // PANEL_MAX_BYTES).  Their traffic is 2 bytes per (query, key) pair at any
+  // D, while the recomputation they replace scales with D: at D = 64 the
+  // recomputing dQ pass is faster (measured on MI355X), so it is kept there.
   size_t panel_bytes() const { return 2 * bh() * panel_head(N, causal); }
-  bool panels_ok() const { return bf16() && panel_bytes() <= PANEL_MAX_BYTES; }
+  bool panels_ok() const { return bf16() && D == 128 && panel_bytes() <= PANEL_MAX_BYTES; }
   static constexpr size_t PANEL_MAX_BYTES = (size_t)16 << 30;
 };
 

@@ -805,10 +805,12 @@ void launch_fwd_mfma(const MfmaParams& p, hipStream_t s) {
   if (nb > 0) RA_LAUNCH(fwd_kernel, nb);
 }
 void launch_dq_mfma(const MfmaParams& p, hipStream_t s) {
-  if (p.dsp) {  // dense attention with the dS panels written by the dK/dV pass
+  if (p.dsp) {  // dense attention with the dS panels written by the dK/dV pass (D = 128)
     const int nb = dq_panel_blocks(p);
     const dim3 grid((unsigned)nb), block(256);
-    if (nb > 0) RA_LAUNCH1(dq_panel_kernel);
+    if (nb <= 0) return;
+    if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dq_panel_kernel<128, false>), grid, block, 0, s, p);
     return;
   }
   const int nb = fwd_blocks(p);
@@ -818,9 +820,14 @@ void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s) {
   const int nb = dkdv_blocks(p);
   if (nb <= 0) return;
   const dim3 grid((unsigned)nb), block(256);
-  if (p.bmask) RA_LAUNCH1(dkdv_kernel, true, false);
-  else if (p.dsp) RA_LAUNCH1(dkdv_kernel, false, true);
-  else RA_LAUNCH1(dkdv_kernel, false, false);
+  if (p.bmask) {
+    RA_LAUNCH1(dkdv_kernel, true, false);
+  } else if (p.dsp) {  // D = 128 only (the library sets panels for no other D)
+    if (p.causal) hipLaunchKernelGGL((dkdv_kernel<128, true, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<128, false, false, true>), grid, block, 0, s, p);
+  } else {
+    RA_LAUNCH1(dkdv_kernel, false, false);
+  }
 }
 
 }  // namespace ra

@@ -90,8 +90,8 @@ int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* 
                   int N, int D, int dtype, double base, const float* alpha, int causal,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace for rope_attn_bwd; 0 on invalid arguments.  With bf16 inputs it
- * includes the dS panels: the dK/dV pass stores dS = P o (dP - D_i) in fp16
+/* Workspace for rope_attn_bwd; 0 on invalid arguments.  With bf16 inputs and
+ * D = 128 it includes the dS panels: the dK/dV pass stores dS = P o (dP - D_i) in fp16
  * there (about B*H*N^2 bytes under the causal mask, 2*B*H*N^2 without it)
  * and dQ is then one product dS K~ instead of a pass that recomputes the
  * scores and dP.  The panels are included when they take at most 16 GiB;
@@ -102,7 +102,8 @@ int rope_attn_fwd(const void* q, const void* k, const void* v, float* o, float* 
 size_t rope_attn_bwd_workspace_bytes(int B, int H, int N, int D, int dtype, int causal);
 
 /* The smallest workspace rope_attn_bwd accepts (no dS panels); equal to
- * rope_attn_bwd_workspace_bytes for fp32 inputs and when the panels would
+ * rope_attn_bwd_workspace_bytes for fp32 inputs, for D = 64 (where
+ * recomputing the scores is the faster dQ pass) and when the panels would
  * exceed 16 GiB; 0 on invalid arguments. */
 size_t rope_attn_bwd_workspace_bytes_min(int B, int H, int N, int D, int dtype, int causal);
 

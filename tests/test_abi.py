@@ -139,12 +139,14 @@ def test_workspace_panels(lib):
         pb = _panel_bytes(B, H, N, causal)
         assert full - lo == (pb + 255) // 256 * 256, (B, H, N, causal)
         assert lo > lib.rope_attn_fwd_workspace_bytes(B, H, N, 128, 1, causal)
-    # fp32 inputs never use panels; above 16 GiB of panels neither does bf16
+    # fp32 inputs and D = 64 never use panels; above 16 GiB of panels neither does bf16
+    assert (lib.rope_attn_bwd_workspace_bytes(1, 8, 32768, 64, 1, 1)
+            == lib.rope_attn_bwd_workspace_bytes_min(1, 8, 32768, 64, 1, 1))
     assert (lib.rope_attn_bwd_workspace_bytes(1, 4, 4096, 64, 0, 1)
             == lib.rope_attn_bwd_workspace_bytes_min(1, 4, 4096, 64, 0, 1))
     assert _panel_bytes(1, 64, 32768, 1) > 16 << 30
-    assert (lib.rope_attn_bwd_workspace_bytes(1, 64, 32768, 64, 1, 1)
-            == lib.rope_attn_bwd_workspace_bytes_min(1, 64, 32768, 64, 1, 1))
+    assert (lib.rope_attn_bwd_workspace_bytes(1, 64, 32768, 128, 1, 1)
+            == lib.rope_attn_bwd_workspace_bytes_min(1, 64, 32768, 128, 1, 1))
     assert lib.rope_attn_bwd_workspace_bytes_min(1, 1, 16, 96, 1, 1) == 0   # bad D
 
 
