@@ -170,17 +170,13 @@ struct TileDMA {
   // src is the head's plane; byte offsets within a plane fit 32 bits
   // (N D 2 <= 2^32 for every accepted shape), so the address is a scalar
   // base plus one zero-extended 32-bit lane offset: the scalar-base form
-  template <bool NT = false>
   __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0, int N) const {
     const char* base = reinterpret_cast<const char*>(src);
     const uint32_t rb = (uint32_t)r0 * (uint32_t)(2 * D);
     if (r0 + ROWS <= N) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        if (issued(i)) {
-          if constexpr (NT) lds_copy16_nt(base, rb + off[i], tile + (wave + 4 * i) * 512);
-          else lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
-        }
+        if (issued(i)) lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
       }
     } else {
 #pragma unroll
