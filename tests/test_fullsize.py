@@ -24,14 +24,17 @@ def _wedge(x, g):
     return x[..., 0::2] * g[..., 1::2] - x[..., 1::2] * g[..., 0::2]
 
 
-@pytest.mark.parametrize("name,all_heads_dalpha", [
-    ("layer_2k", True), ("long_8k", True), ("train_4k", False), ("vlong_32k", False)])
-def test_full_size(name, all_heads_dalpha):
+@pytest.mark.parametrize("name,all_heads_dalpha,ws", [
+    ("layer_2k", True, "bwd"), ("long_8k", True, "bwd"), ("train_4k", False, "bwd"),
+    ("vlong_32k", False, "bwd"), ("long_8k", False, "bwd_min")])
+def test_full_size(name, all_heads_dalpha, ws):
+    """ws: the backward workspace query; "bwd" takes the dS panels where they
+    apply (D = 128), "bwd_min" the pass that recomputes the scores for dQ."""
     from oracle import ref
     wl = W.get(name)
     inp = W.make_inputs(wl)
-    print(f"{name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D}", flush=True)
-    got = Hn.run_gpu(inp)
+    print(f"{name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D} workspace {ws}", flush=True)
+    got = Hn.run_gpu(inp, ws=ws)
     for n in ("O", "LSE", "dQ", "dK", "dV", "dalpha"):
         assert np.isfinite(got[n]).all(), n
     q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))

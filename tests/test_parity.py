@@ -94,6 +94,14 @@ def test_bf16_recomputing_dq(name, H, N, causal):
     _check(W.make_inputs(wl), causal=causal, ws="bwd_min")
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(2, 3, 600, False), (3, 1, 1000, True), (2, 2, 513, True)])
+def test_bf16_panels_batches(B, H, N, causal):
+    """The dS panels with several sequences and heads (panel offsets per
+    (b, h)), ragged lengths spanning several 256-query panels, both masks."""
+    wl = dataclasses.replace(W.get("long_8k", B=B, H=H, N=N, seed=900 + N), causal=causal)
+    _check(W.make_inputs(wl), causal=causal)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_panels_and_recomputation_agree(causal):
     """The two dQ passes on the same inputs: dK and dV come from the same
