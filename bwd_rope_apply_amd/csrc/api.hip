@@ -125,7 +125,8 @@ Layout layout(Shape s, bool bwd, bool panels = false) {
   s.blocks = 0;
   L.theta = up(sizeof(double) * (s.D / 2));
   L.cs = up(sizeof(float2) * (size_t)s.N * (s.D / 2));
-  const size_t h16 = up(2 * s.elems());
+  // fp16 planes: every head's rows, then PLANE_PAD_ROWS zero rows
+  const size_t h16 = up(2 * (s.elems() + (size_t)PLANE_PAD_ROWS * s.D));
   if (s.bf16()) {
     L.qh = L.kh = L.vh = h16;
     if (bwd) L.doh = h16;

@@ -66,6 +66,13 @@ __host__ __device__ inline size_t panel_head(int N, int causal) {
   return panel_off(n_panels(N), N, causal);
 }
 
+// The fp16 operand planes in the workspace carry PLANE_PAD_ROWS zero rows
+// after their last head, so a streamed tile that starts below N never reads
+// past the plane: the tile copies need no per-row clamp.  Rows at or past N
+// of a head read the next head's rows (or the zero pad); every use of them
+// is masked or multiplied by an exact zero, and all of them are finite.
+constexpr int PLANE_PAD_ROWS = 64;
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 

@@ -317,16 +317,16 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
 
   TileDMA<D, BN> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, walk.cur, p.N);
-  dma.load(Vs, vh, walk.cur, p.N);
+  dma.load(Ks, kh, walk.cur);
+  dma.load(Vs, vh, walk.cur);
   wait_lds_copies();
   __syncthreads();
   auto step = [&](int kt, auto masked) {
     const int k0 = walk.cur;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
     if (kt + 1 < n_kt) {
-      dma.load(Ks + nxt, kh, walk.next, p.N);
-      dma.load(Vs + nxt, vh, walk.next, p.N);
+      dma.load(Ks + nxt, kh, walk.next);
+      dma.load(Vs + nxt, vh, walk.next);
     }
     walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
@@ -422,8 +422,8 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
 
   TileDMA<D, KB> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, walk.cur, p.N);
-  dma.load(Vs, vh, walk.cur, p.N);
+  dma.load(Ks, kh, walk.cur);
+  dma.load(Vs, vh, walk.cur);
   wait_lds_copies();
   __syncthreads();
   const int klim = CAUSAL ? min(qrow, p.N - 1) : p.N - 1;
@@ -431,8 +431,8 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
     const int k0 = walk.cur;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
     if (kt + 1 < n_kt) {
-      dma.load(Ks + nxt, kh, walk.next, p.N);
-      dma.load(Vs + nxt, vh, walk.next, p.N);
+      dma.load(Ks + nxt, kh, walk.next);
+      dma.load(Vs + nxt, vh, walk.next);
     }
     walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
@@ -537,8 +537,8 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   // one step's tiles; wave j < NMB also copies the row scalars of 32-row
   // group j (lane i -> float i; qs0 is a multiple of 32)
   auto load_rows = [&](int r0, int buf) {
-    dma.load(Qs + buf * TILE, qh, r0, p.N);
-    dma.load(Ds + buf * TILE, doh, r0, p.N);
+    dma.load(Qs + buf * TILE, qh, r0);
+    dma.load(Ds + buf * TILE, doh, r0);
     if (dma.wave < NMB)
       lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane_here(), rsl + buf * 2 * QB + dma.wave * 64);
   };
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   };
   auto load = [&](int kt) {
     const int b = kt % NS;
-    dmk.load(Ks + b * TK, kh, kt * DQP_KB, p.N);
+    dmk.load(Ks + b * TK, kh, kt * DQP_KB);
     // the panel tile: 1 KiB blocks wave + 4 i, lane l at byte 16 l
     const uint32_t tb = (uint32_t)kt * (uint32_t)(2 * DQP_TS);
 #pragma unroll

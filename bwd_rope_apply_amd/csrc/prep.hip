@@ -141,6 +141,15 @@ __global__ void prep_kernel(PrepParams p) {
       if (p.kh && p.klo) store8lo(p.klo + lo, xk);
     }
   }
+  // the planes' zero pad rows after the last head (PLANE_PAD_ROWS x D)
+  if (gid < (long)PLANE_PAD_ROWS * cpr) {
+    const size_t e = (size_t)p.BH * p.N * p.D + (size_t)gid * 8;
+    const half8 z = {};
+    if (p.qh) *reinterpret_cast<half8*>(p.qh + e) = z;
+    if (p.kh) *reinterpret_cast<half8*>(p.kh + e) = z;
+    if (p.vh) *reinterpret_cast<half8*>(p.vh + e) = z;
+    if (p.doh) *reinterpret_cast<half8*>(p.doh + e) = z;
+  }
   if (p.doh || p.drow) {
     float acc = 0.f;
     if (live) {
@@ -172,7 +181,8 @@ __global__ void prep_kernel(PrepParams p) {
 }
 
 void launch_prep(const PrepParams& p, hipStream_t s) {
-  const long total = (long)p.BH * p.N * (p.D / 8);
+  // every chunk of every row, and at least the planes' pad chunks
+  const long total = max((long)p.BH * p.N * (p.D / 8), (long)PLANE_PAD_ROWS * (p.D / 8));
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   if (p.bf16) hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(prep_kernel<false>, grid, block, 0, s, p);

@@ -98,9 +98,10 @@ __device__ __forceinline__ int sig_inv(int P) {
 // loads a dummy chunk (row 0), so every lane of an issued block loads and no
 // per-lane branch is needed.  Each lane's byte offset from the tile's first
 // row is computed once; a step adds the tile's row base in scalar registers.
-// Rows at or past N are clamped to N - 1 (masked downstream) on the one
-// path that needs it.  Callers wait for the copies (wait_lds_copies) before
-// the barrier that publishes the tile.
+// Rows past the head's last row are read as they are (the next head's rows
+// or the plane's zero pad, see PLANE_PAD_ROWS); the tiles' consumers mask
+// them.  Callers wait for the copies (wait_lds_copies) before the barrier
+// that publishes the tile.
 // One lane-wise 16-byte (or 4-byte) global -> LDS copy: lane i writes LDS
 // bytes [lds + size i, lds + size (i + 1)) from gbase + voff (gbase and lds
 // uniform).  It is the same global_load_lds instruction the compiler's
@@ -146,6 +147,7 @@ __device__ __forceinline__ void lds_copy4(const void* gbase, uint32_t voff, cons
 
 template <int D, int ROWS>
 struct TileDMA {
+  static_assert(ROWS <= PLANE_PAD_ROWS, "a tile starting below N must end inside the padded plane");
   static constexpr int RB = (D + 8) * 2;                 // bytes per physical row
   static constexpr int BYTES = ROWS * RB;
   static constexpr int NBLK = (BYTES + 1023) / 1024;
@@ -167,26 +169,17 @@ struct TileDMA {
   __device__ __forceinline__ bool issued(int i) const { return i < NBLK / 4 || wave + 4 * i < NBLK; }
   // copy instructions this wave issues per load (uniform)
   __device__ __forceinline__ int count() const { return NBLK / 4 + (wave < NBLK % 4 ? 1 : 0); }
-  // src is the head's plane; byte offsets within a plane fit 32 bits
-  // (N D 2 <= 2^32 for every accepted shape), so the address is a scalar
-  // base plus one zero-extended 32-bit lane offset: the scalar-base form
-  __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0, int N) const {
+  // src is the head's rows in a padded plane and r0 < N, so the tile ends
+  // inside the plane.  Byte offsets from src fit 32 bits (r0 is a multiple
+  // of ROWS below N <= 2^24, and 2 D <= 256),
+  // so the address is a scalar base plus one zero-extended 32-bit lane
+  // offset: the scalar-base form.
+  __device__ __forceinline__ void load(half_t* tile, const half_t* src, int r0) const {
     const char* base = reinterpret_cast<const char*>(src);
     const uint32_t rb = (uint32_t)r0 * (uint32_t)(2 * D);
-    if (r0 + ROWS <= N) {
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        if (issued(i)) lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        if (issued(i)) {
-          const int row = r0 + (int)(off[i] / (2 * D));
-          const uint32_t o = (uint32_t)min(row, N - 1) * (uint32_t)(2 * D) + off[i] % (2 * D);
-          lds_copy16(base, o, tile + (wave + 4 * i) * 512);
-        }
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      if (issued(i)) lds_copy16(base, rb + off[i], tile + (wave + 4 * i) * 512);
     }
   }
 };
