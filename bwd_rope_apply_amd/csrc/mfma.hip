@@ -19,15 +19,21 @@ namespace ra {
 namespace {
 
 // Tiling (compile-time; the defaults are the measured best on MI355X):
-//   *_WPS   waves per SIMD the register budget is sized for (2 lets one
-//           wave's softmax VALU work overlap the other wave's MFMAs)
+//   *_WPS   waves per SIMD the register budget is sized for (more waves
+//           let one wave's softmax VALU work overlap another's MFMAs; the
+//           512 VGPRs of a SIMD lane are shared among them)
 //   *_BN    rows of the streamed operand per loop step (multiple of 32)
 //   FWD_NB  32-row query blocks per forward wave
+//   FWD_MB  32-key blocks per forward step (1: 32-key tiles, whose smaller
+//           registers and LDS allow 3 waves per SIMD)
 #ifndef RA_FWD_NB
 #define RA_FWD_NB 1
 #endif
 #ifndef RA_FWD_WPS
-#define RA_FWD_WPS 2
+#define RA_FWD_WPS 3
+#endif
+#ifndef RA_FWD_MB
+#define RA_FWD_MB 1        // 32-key blocks per forward step
 #endif
 #ifndef RA_FWD_SEED
 #define RA_FWD_SEED 0      // 1: fold the running max into the score accumulators
@@ -49,8 +55,8 @@ namespace {
 #endif
 
 
-// One 64-key step of the forward for one wave owning NB blocks of 32 query
-// rows: scores, online softmax, O += P V.  Every K~ and V fragment read from
+// One step of the forward (MB blocks of 32 keys) for one wave owning NB
+// blocks of 32 query rows: scores, online softmax, O += P V.  Every K~ and V fragment read from
 // LDS feeds NB products.  Q~ carries the factor log2(e)/sqrt(D), so scores
 // are in log2 units.  m is the reference maximum the running sum l and O
 // are relative to; it is seeded into the score accumulators (so they hold
@@ -60,18 +66,18 @@ namespace {
 // klim[nb] (causal diagonal, ragged tail).
 constexpr float RESCALE_SLACK = 8.f;
 
-template <int D, int NB, bool MASK>
+template <int D, int NB, bool MASK, int MB = 2>
 __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l,
                                          const half_t* Ks, const half_t* Vs,
                                          const half8 (*qf)[D / 16], int k0, const int* klim,
                                          int lane) {
   const int l32 = lane & 31, g = lane >> 5;
-  f32x16 s[NB][2];
+  f32x16 s[NB][MB];
   float base[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) base[nb] = m[nb] == -INFINITY ? 0.f : m[nb];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -85,12 +91,12 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
       for (int nb = 0; nb < NB; ++nb) s[nb][mb] = mfma(a, qf[nb][t], s[nb][mb]);
     }
   }
-  half8 pf[NB][4];
+  half8 pf[NB][2 * MB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = RA_FWD_SEED ? s[nb][mb][r] : s[nb][mb][r] - base[nb];
@@ -113,14 +119,14 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb) o[nb][cb] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nb][mb][r] -= shift;
       }
     }
     float ls = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = exp2_fast(s[nb][mb][r]);
@@ -129,13 +135,13 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
       }
     }
     l[nb] += ls;
-    to_frags(s[nb], pf[nb]);
+    to_frags<MB>(s[nb], pf[nb]);
   }
   // O^T[c][q] += V^T[c][key] P^T[key][q]: V^T fragments by transposed reads
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2 * MB; ++t) {
       const half8 a = tr_frag<D>(Vs, t, cb, lane);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nb][cb] = mfma(a, pf[nb][t], o[nb][cb]);
@@ -246,16 +252,18 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
 }
 
 // ------------------------------------------------------------------ forward
-// Workgroup = 256 query rows of one head (4 waves x 64 rows, two 32-row
-// blocks per wave); the loop streams 64-key tiles of K~ and V through
-// double-buffered LDS, the next tile's global loads in flight while the
-// current tile is computed.  Rows below the exact corner are skipped.
+// Workgroup = 128 FWD_NB query rows of one head (4 waves x 32 FWD_NB rows);
+// the loop streams FBN-key tiles of K~ and V through double-buffered LDS,
+// the next tile's copies in flight while the current tile is computed.
+// Rows below the exact corner are skipped.
 constexpr int FWD_NB = RA_FWD_NB;
 constexpr int FWD_BM = 4 * 32 * FWD_NB;
+constexpr int FWD_MB = RA_FWD_MB;
+constexpr int FBN = 32 * FWD_MB;   // keys per forward step
 
 template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
-  constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, BN>::ALLOC, NB = FWD_NB;
+  constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, FBN>::ALLOC, NB = FWD_NB;
   __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
   __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the key blocks, ascending
@@ -297,25 +305,25 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
   // the steps that start below N).
   int n_kt, split;
   if constexpr (BL) {
-    static_assert(FWD_BM == BLK && BLK == 2 * BN, "one query block per workgroup");
+    static_assert(FWD_BM == BLK && BLK % FBN == 0, "one query block per workgroup");
     if (w == 0) {
       const int c = row_blocks(p.bmask + ((size_t)bh * p.nb + t) * p.W, p.nb, blist, lane);
       if (lane == 0) bcount = c;
     }
     __syncthreads();
     const int last = blist[bcount - 1];
-    const int rows = min(BLK, p.N - last * BLK), steps = (rows + BN - 1) / BN;
-    n_kt = 2 * (bcount - 1) + steps;
+    const int rows = min(BLK, p.N - last * BLK), steps = (rows + FBN - 1) / FBN;
+    n_kt = BLK / FBN * (bcount - 1) + steps;
     split = ((CAUSAL && last == t) || rows < BLK) ? n_kt - steps : n_kt;
   } else {
-    const int nk = (p.N + BN - 1) / BN;
-    n_kt = CAUSAL ? min(nk, (q0 + FWD_BM + BN - 1) / BN) : nk;
-    split = min(n_kt, min(CAUSAL ? q0 / BN : nk, p.N / BN));
+    const int nk = (p.N + FBN - 1) / FBN;
+    n_kt = CAUSAL ? min(nk, (q0 + FWD_BM + FBN - 1) / FBN) : nk;
+    split = min(n_kt, min(CAUSAL ? q0 / FBN : nk, p.N / FBN));
   }
-  Walk<BN, BL> walk;
+  Walk<FBN, BL> walk;
   walk.init(blist, 0, n_kt);
 
-  TileDMA<D, BN> dma;
+  TileDMA<D, FBN> dma;
   dma.init(lane, w);
   dma.load(Ks, kh, walk.cur);
   dma.load(Vs, vh, walk.cur);
@@ -331,7 +339,8 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
     walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (active && !(CAUSAL && k0 > wlast))  // skip tiles wholly above this wave's rows
-      fwd_tile<D, NB, decltype(masked)::value>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim, lane);
+      fwd_tile<D, NB, decltype(masked)::value, FWD_MB>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim,
+                                                       lane);
     wait_lds_copies();
     __syncthreads();
     walk.advance(kt);
