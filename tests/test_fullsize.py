@@ -76,3 +76,24 @@ def test_full_size(name, all_heads_dalpha, ws):
         e = Hn.err_rms(got["dalpha"], prop)
         print(name, "dalpha vs its definition on the GPU's dQ, dK:", e, flush=True)
         assert e <= 1e-3
+
+
+def test_one_head_65536():
+    """One head at N = 65536, D = 128 (the longest sequence block lists
+    accept), long_8k's distributions: the dS panels alone take 4.3 GB here,
+    so panel offsets pass 2^32 bytes.  Every output of the head against the
+    oracle under the bf16 bar, and dalpha against the oracle's."""
+    from oracle import ref
+    wl = W.get("long_8k", B=1, H=1, N=65536, seed=4242)
+    inp = W.make_inputs(wl)
+    print(f"{wl.name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D}", flush=True)
+    got = Hn.run_gpu(inp)
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    o, lse = ref.ref_fwd(q, k, v, wl.base, inp.alpha, wl.causal)
+    dq, dk, dv, da = ref.ref_bwd(q, k, v, o, do, lse, wl.base, inp.alpha, wl.causal)
+    errs = {n: Hn.err_rms(got[n], r) for n, r in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv),
+                                                   ("dalpha", da))}
+    errs["LSE_abs"] = float(np.abs(got["LSE"] - lse).max())
+    print(errs, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)
