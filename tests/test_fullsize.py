@@ -97,3 +97,32 @@ def test_one_head_65536():
     print(errs, flush=True)
     for n, e in errs.items():
         assert e <= TOL, (n, e)
+
+
+def test_full_size_noncausal():
+    """long_8k at full size without the causal mask: every key visible, so
+    the dS panels hold all N^2 pairs per head (4.3 GB).  Two complete heads
+    against the oracle under the bf16 bar, rotational balance on all."""
+    import dataclasses
+    from oracle import ref
+    wl = dataclasses.replace(W.get("long_8k"), causal=False)
+    inp = W.make_inputs(wl)
+    got = Hn.run_gpu(inp, causal=False)
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    refs = {n: [] for n in ("O", "dQ", "dK", "dV")}
+    gots = {n: [] for n in refs}
+    for b, h in ((0, 0), (wl.B - 1, wl.H - 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o, lse = ref.ref_fwd(q[sl], k[sl], v[sl], wl.base, inp.alpha, False)
+        dq, dk, dv, _ = ref.ref_bwd(q[sl], k[sl], v[sl], o, do[sl], lse, wl.base, inp.alpha, False)
+        for n, r in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+            refs[n].append(r[0, 0])
+            gots[n].append(got[n][b, h])
+    errs = {n: Hn.err_rms(np.stack(gots[n]), np.stack(refs[n])) for n in refs}
+    print("long_8k non-causal", errs, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)
+    wq = _wedge(q, got["dQ"]).sum(axis=2)
+    wk = _wedge(k, got["dK"]).sum(axis=2)
+    scale = np.abs(_wedge(q, got["dQ"])).sum(axis=2).max()
+    assert np.abs(wq + wk).max() <= 1e-3 * scale
