@@ -28,9 +28,10 @@ __host__ __device__ inline int corner_rows(int N) {
   return CORNER_UNIT * (units < 1 ? 1 : units);
 }
 
-// Backward row scalars in 32-row groups: [LSE * log2(e) x 32 | D x 32] per
-// group, one spare group after the last; rows >= N hold (+inf, 0) so that
-// their P = exp2(S - LSE2) is exactly 0.
+// Backward row scalars in 32-row groups: [-LSE * log2(e) x 32 | -D x 32] per
+// group (negated: they seed the dK/dV products' accumulators), one spare
+// group after the last; rows >= N hold (-inf, 0) so that their
+// P = exp2(S - LSE2) is exactly 0.
 __host__ __device__ inline int rs_groups(int N) { return (N + 31) / 32 + 1; }
 
 // Block-list attention: query and key blocks of BLK rows; a visibility

@@ -187,10 +187,12 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const half_t* Ks, const hal
 // One step of dK, dV for one wave over 32 NMB queries (this lane's key
 // along n): P = exp(S - LSE), dV += P^T dO, dP = dO V^T, dS = P o (dP - D),
 // dK~ += dS^T Q~.  MASK hides queries before this lane's key.  rsc holds
-// the step's row scalars, 32-row groups of [LSE * log2(e) | D]; vrow points
-// at this lane's V row in the stationary LDS tile.  DS also hands out the
-// fp16 dS row of this lane's key (its 32 NMB queries, 8 per 16-byte chunk)
-// in ds_out, zeros for a key at or past N.
+// the step's row scalars, 32-row groups of [-LSE * log2(e) | -D]: they seed
+// the score and dP accumulators (each accumulator row is one query), so
+// the products come out as S - LSE and dP - D.  vrow points at this lane's
+// V row in the stationary LDS tile.  DS also hands out the fp16 dS row of
+// this lane's key (its 32 NMB queries, 8 per 16-byte chunk) in ds_out,
+// zeros for a key at or past N.
 template <int D, int NMB, bool MASK, bool DS = false>
 __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* Qs,
                                           const half_t* Ds, const float* rsc, const half8* kf,
@@ -198,47 +200,46 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
                                           half8* ds_out = nullptr, bool key_ok = true) {
   const int l32 = lane & 31, g = lane >> 5;
   f32x16 s[NMB], dp[NMB];
-  scores<D, NMB>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* lr = rsc + 64 * mb + 16 * h + 8 * g;
+      const float4 la = *reinterpret_cast<const float4*>(lr);
+      const float4 lb = *reinterpret_cast<const float4*>(lr + 4);
+      const float4 da = *reinterpret_cast<const float4*>(lr + 32);
+      const float4 db = *reinterpret_cast<const float4*>(lr + 36);
+      const float lv8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[mb][8 * h + e] = lv8[e];
+        dp[mb][8 * h + e] = dv8[e];
+      }
+    }
+  }
+  scores_add<D, NMB>(s, Qs, kf, l32, g);   // queries along m, this lane's key along n
   // P first: it needs only the scores, so its exps can issue between the
   // dP products below
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ql = 32 * mb + 16 * h + 8 * g;
-      const float* lr = rsc + 64 * mb + 16 * h + 8 * g;
-      const float4 la = *reinterpret_cast<const float4*>(lr);
-      const float4 lb = *reinterpret_cast<const float4*>(lr + 4);
-      const float lv8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * h + e;
-        float pr = exp2_fast(s[mb][r] - lv8[e]);
-        if (MASK) pr = key > r0 + ql + e ? 0.f : pr;
-        s[mb][r] = pr;
-      }
+    for (int r = 0; r < 16; ++r) {
+      float pr = exp2_fast(s[mb][r]);
+      if (MASK) pr = key > r0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7) ? 0.f : pr;
+      s[mb][r] = pr;
     }
   }
   {
     half8 vl[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) vl[t] = *reinterpret_cast<const half8*>(vrow + 16 * t);
-    scores<D, NMB>(dp, Ds, vl, l32, g);
+    scores_add<D, NMB>(dp, Ds, vl, l32, g);
   }
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float* lr = rsc + 64 * mb + 16 * h + 8 * g;
-      const float4 da = *reinterpret_cast<const float4*>(lr + 32);
-      const float4 db = *reinterpret_cast<const float4*>(lr + 36);
-      const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * h + e;
-        dp[mb][r] = s[mb][r] * (dp[mb][r] - dv8[e]);
-      }
-    }
+    for (int r = 0; r < 16; ++r) dp[mb][r] = s[mb][r] * dp[mb][r];
   }
   half8 pf[2 * NMB], sf[2 * NMB];
   to_frags<NMB>(s, pf);

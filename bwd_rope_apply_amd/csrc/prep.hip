@@ -166,11 +166,11 @@ __global__ void prep_kernel(PrepParams p) {
         if (p.rs) {
           const int G = rs_groups(p.N);
           float* rsh = p.rs + (size_t)(row / p.N) * G * 64;
-          rsh[(pos >> 5) * 64 + (pos & 31)] = p.lse[row] * LOG2E;
-          rsh[(pos >> 5) * 64 + 32 + (pos & 31)] = acc;
+          rsh[(pos >> 5) * 64 + (pos & 31)] = -(p.lse[row] * LOG2E);
+          rsh[(pos >> 5) * 64 + 32 + (pos & 31)] = -acc;
           if (pos == p.N - 1) {  // pad rows up to the end of the spare group
             for (int r = p.N; r < 32 * G; ++r) {
-              rsh[(r >> 5) * 64 + (r & 31)] = INFINITY;
+              rsh[(r >> 5) * 64 + (r & 31)] = -INFINITY;
               rsh[(r >> 5) * 64 + 32 + (r & 31)] = 0.f;
             }
           }
