@@ -270,7 +270,8 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
   __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the key blocks, ascending
   __shared__ int bcount;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int ntiles = (p.N + FWD_BM - 1) / FWD_BM, t0 = p.corner / FWD_BM;
   int bh, t;
@@ -386,7 +387,8 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
   __shared__ int bcount;
   __shared__ float red[4 * (D / 2)];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int ntiles = (p.N + BM - 1) / BM, t0 = p.corner / BM;
   int bh, t;
@@ -493,7 +495,9 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   __shared__ uint32_t bcol[BL ? MAX_BLOCKS / 32 : 1];
   __shared__ int bcount;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  // the wave index as a scalar: per-wave skips and panel addresses stay uniform
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int ntiles = (p.N + BM - 1) / BM;
   int bh, t;
@@ -642,18 +646,15 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
 }
 
 // ------------------------------------------------------------------ dQ from the dS panels
-// B fragment (8 keys of one query per lane, as the score registers give it)
-// from a 32-key panel tile in LDS, query block c (32 queries), k step ts:
-// in each 16-lane group the 16 lanes point at 4 keys x 16 queries of the
+// B fragments (8 keys of one query per lane, as the score registers give
+// it) from a 32-key panel tile in LDS: query block c (32 queries), k step
+// ts at lane offset + 1024 c + 256 ts, two transposed reads 64 halfs apart.
+// In each 16-lane group the 16 lanes point at 4 keys x 16 queries of the
 // block's half b (4 consecutive queries each, 128 contiguous bytes: no bank
 // conflict) and the transposing read hands lane j query j's 4 keys.
-__device__ __forceinline__ half8 panel_frag(const half_t* tile, int c, int ts, int lane) {
+__device__ __forceinline__ int panel_lane_offset(int lane) {
   const int s16 = lane & 15, b = (lane >> 4) & 1, g = lane >> 5;
-  const half_t* p = tile + c * 1024 + b * 512 + (16 * ts + 8 * g + (s16 >> 2)) * 16 + 4 * (s16 & 3);
-  const s16x4 lo = ds_read_tr(p), hi = ds_read_tr(p + 4 * 16);
-  typedef __attribute__((ext_vector_type(8))) short s16x8;
-  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(half8, both);
+  return b * 512 + (8 * g + (s16 >> 2)) * 16 + 4 * (s16 & 3);
 }
 
 // dQ~ = dS K~ over the panels the dK/dV pass wrote: a plain product, no
@@ -684,7 +685,8 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   __shared__ __attribute__((aligned(16))) half_t Ss[NS * TS];
   __shared__ float red[4 * (D / 2)];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int np = n_panels(p.N), t0 = p.corner / PANEL;
   int bh, t;
@@ -709,7 +711,9 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   }
   TileDMA<D, DQP_KB> dmk;
   dmk.init(lane, w);
-  const int wave = __builtin_amdgcn_readfirstlane(w);
+  const int wave = w;
+  // this lane's fragment offsets in a ring slot (its wave's query blocks 2w, 2w + 1)
+  const int pf_lane = 2048 * w + panel_lane_offset(lane), tr_lane = tr_lane_offset<D>(lane);
   // Copies this wave issues per tile: KLO or KLO + 1 for K~, 4 for the panel.
   // Every outstanding vector memory operation of the loop is such a copy, so
   // "tile i landed" is "at most (copies per tile) x (tiles issued after i)
@@ -740,20 +744,32 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * DQP_KB;
-    const int ck = (kt % NS) * TK, cs = (kt % NS) * TS;
+    // ring slot offsets as opaque scalars: the fragment addresses are then one
+    // add each, not offsets the compiler derives from kt per read
+    const int slot = __builtin_amdgcn_readfirstlane(kt % NS);
+    const int ck = slot * TK, cs = slot * TS;
     // into the buffer every wave finished reading before the last barrier
     if (kt + NS - 1 < n_kt) load(kt + NS - 1);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tiles' copies ahead of the compute
     if (active && !(CAUSAL && k0 > wrow0 + 63)) {
+      // every fragment of the step first (one address add per operand, the
+      // rest in the reads' offsets), then the products
+      const half_t* pb = Ss + cs + pf_lane;
+      const half_t* kb = Ks + ck + tr_lane;
+      half8 bf[DQP_KB / 16][2], af[DQP_KB / 16][CB];
 #pragma unroll
       for (int ts = 0; ts < DQP_KB / 16; ++ts) {
-        const half8 b0 = panel_frag(Ss + cs, 2 * w, ts, lane);
-        const half8 b1 = panel_frag(Ss + cs, 2 * w + 1, ts, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[ts][j] = tr_pair<64>(pb + 1024 * j + 256 * ts);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) af[ts][cb] = tr_pair<8 * (D + 8)>(kb + 16 * ts * (D + 8) + 32 * cb);
+      }
+#pragma unroll
+      for (int ts = 0; ts < DQP_KB / 16; ++ts) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const half8 a = tr_frag<D>(Ks + ck, ts, cb, lane);
-          acc[0][cb] = mfma(a, b0, acc[0][cb]);
-          acc[1][cb] = mfma(a, b1, acc[1][cb]);
+          acc[0][cb] = mfma(af[ts][cb], bf[ts][0], acc[0][cb]);
+          acc[1][cb] = mfma(af[ts][cb], bf[ts][1], acc[1][cb]);
         }
       }
     }

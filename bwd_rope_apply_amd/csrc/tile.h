@@ -354,6 +354,23 @@ __device__ __forceinline__ s16x4 ds_read_tr(const half_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Two transposed reads, at p and p + HI halfs, as one 8-value fragment.
+template <int HI>
+__device__ __forceinline__ half8 tr_pair(const half_t* p) {
+  const s16x4 lo = ds_read_tr(p), hi = ds_read_tr(p + HI);
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(half8, both);
+}
+
+// This lane's part of the address of tr_frag's reads (halfs from the tile):
+// the rest, 16 t (D + 8) + 32 cb, is the same for every lane.
+template <int D>
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int s16 = lane & 15, g = lane >> 5, b = (lane >> 4) & 1;
+  return sig(8 * g + (s16 >> 2)) * (D + 8) + 16 * b + 4 * (s16 & 3);
+}
+
 // A-operand fragment of X^T for k step t and column block cb, X a [BN][D]
 // tile in LDS (two transposed reads).
 template <int D>
@@ -361,12 +378,7 @@ __device__ __forceinline__ half8 tr_frag(const half_t* lds, int t, int cb, int l
   // logical rows 16t + 8g + 4h + e, e = s16 >> 2 (h = 0, 1), columns
   // 32cb + 16 b + 4 (s16 & 3): physical row 16t + 8h + sig(8g + e)
   constexpr int LD = D + 8;
-  const int s16 = lane & 15, g = lane >> 5, b = (lane >> 4) & 1;
-  const half_t* p = lds + (sig(8 * g + (s16 >> 2)) + 16 * t) * LD + 32 * cb + 16 * b + 4 * (s16 & 3);
-  const s16x4 lo = ds_read_tr(p), hi = ds_read_tr(p + 8 * LD);
-  typedef __attribute__((ext_vector_type(8))) short s16x8;
-  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(half8, both);
+  return tr_pair<8 * LD>(lds + tr_lane_offset<D>(lane) + 16 * t * LD + 32 * cb);
 }
 
 // acc[cb] += X^T(columns 32cb.., rows = 16-wide k steps) * frag, with X a
