@@ -89,16 +89,22 @@ __device__ __forceinline__ void store8lo(half_t* dst, const float* x) {
 
 // BF16: the input storage (compile time, so that no branch separates a
 // load from its use and every load of a thread issues before the first wait)
+// Grid: x over the chunks of one head (N * D / 8 < 2^28), y and z over the
+// heads (bh = 4096 z + y): the head is a scalar and the position and chunk
+// are shifts, so no thread divides.
+constexpr int PREP_HEADS_Y = 4096;
+
 template <bool BF16>
 __global__ void prep_kernel(PrepParams p) {
-  const int cpr = p.D / 8;                        // chunks per row (8 or 16)
-  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)p.BH * p.N * cpr;
-  const bool live = gid < total;
-  const long row = live ? gid / cpr : 0;          // bh * N + pos
-  const int chunk = (int)(gid % cpr);
-  const int pos = (int)(row % p.N);
-  const size_t e0 = (size_t)row * p.D + (size_t)chunk * 8;
+  const int cshift = p.D == 128 ? 4 : 3;          // chunks per row: 16 or 8
+  const int cpr = 1 << cshift;
+  const int bh = (int)blockIdx.z * PREP_HEADS_Y + (int)blockIdx.y;
+  const int lin = (int)blockIdx.x * 256 + (int)threadIdx.x;   // chunk within the head
+  const bool live = bh < p.BH && lin < (p.N << cshift);
+  const int pos = live ? lin >> cshift : 0;
+  const int chunk = lin & (cpr - 1);
+  const size_t row = (size_t)bh * p.N + pos;      // bh * N + pos
+  const size_t e0 = row * p.D + (size_t)chunk * 8;
   float xq[8], xk[8], xv[8], xd[8];
   Raw8 rq = {}, rk = {}, rv = {}, rd = {};
   float4 oa = {}, ob = {};
@@ -136,14 +142,14 @@ __global__ void prep_kernel(PrepParams p) {
     if (p.kh) store8h(p.kh + e0, xk);
     if (p.vh) store8h(p.vh + e0, xv);
     if (pos < p.rlo) {
-      const size_t lo = ((size_t)(row / p.N) * p.rlo + pos) * p.D + chunk * 8;
+      const size_t lo = ((size_t)bh * p.rlo + pos) * p.D + chunk * 8;
       if (p.qh && p.qlo) store8lo(p.qlo + lo, xq);
       if (p.kh && p.klo) store8lo(p.klo + lo, xk);
     }
   }
   // the planes' zero pad rows after the last head (PLANE_PAD_ROWS x D)
-  if (gid < (long)PLANE_PAD_ROWS * cpr) {
-    const size_t e = (size_t)p.BH * p.N * p.D + (size_t)gid * 8;
+  if (bh == 0 && lin < PLANE_PAD_ROWS * cpr) {
+    const size_t e = (size_t)p.BH * p.N * p.D + (size_t)lin * 8;
     const half8 z = {};
     if (p.qh) *reinterpret_cast<half8*>(p.qh + e) = z;
     if (p.kh) *reinterpret_cast<half8*>(p.kh + e) = z;
@@ -165,7 +171,7 @@ __global__ void prep_kernel(PrepParams p) {
         p.drow[row] = acc;
         if (p.rs) {
           const int G = rs_groups(p.N);
-          float* rsh = p.rs + (size_t)(row / p.N) * G * 64;
+          float* rsh = p.rs + (size_t)bh * G * 64;
           rsh[(pos >> 5) * 64 + (pos & 31)] = -(p.lse[row] * LOG2E);
           rsh[(pos >> 5) * 64 + 32 + (pos & 31)] = -acc;
           if (pos == p.N - 1) {  // pad rows up to the end of the spare group
@@ -182,8 +188,11 @@ __global__ void prep_kernel(PrepParams p) {
 
 void launch_prep(const PrepParams& p, hipStream_t s) {
   // every chunk of every row, and at least the planes' pad chunks
-  const long total = max((long)p.BH * p.N * (p.D / 8), (long)PLANE_PAD_ROWS * (p.D / 8));
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const int per_head = max(p.N * (p.D / 8), PLANE_PAD_ROWS * (p.D / 8));
+  const int hy = min(p.BH, PREP_HEADS_Y);
+  const dim3 grid((unsigned)((per_head + 255) / 256), (unsigned)hy,
+                  (unsigned)((p.BH + PREP_HEADS_Y - 1) / PREP_HEADS_Y)),
+      block(256);
   if (p.bf16) hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(prep_kernel<false>, grid, block, 0, s, p);
 }
