@@ -35,9 +35,6 @@ namespace {
 #ifndef RA_FWD_MB
 #define RA_FWD_MB 1        // 32-key blocks per forward step
 #endif
-#ifndef RA_FWD_SEED
-#define RA_FWD_SEED 0      // 1: fold the running max into the score accumulators
-#endif
 #ifndef RA_DQ_BN
 #define RA_DQ_BN 32
 #endif
@@ -56,33 +53,26 @@ namespace {
 
 
 // One step of the forward (MB blocks of 32 keys) for one wave owning NB
-// blocks of 32 query rows: scores, online softmax, O += P V.  Every K~ and V fragment read from
-// LDS feeds NB products.  Q~ carries the factor log2(e)/sqrt(D), so scores
-// are in log2 units.  m is the reference maximum the running sum l and O
-// are relative to; it is seeded into the score accumulators (so they hold
-// S - m) and only moved when a score exceeds it by more than 2^RESCALE_SLACK,
-// which keeps every P below 2^8 (exact in the arithmetic, since O and l
-// share the reference) and makes the O rescale rare.  MASK hides keys after
-// klim[nb] (causal diagonal, ragged tail).
-constexpr float RESCALE_SLACK = 8.f;
+// blocks of 32 query rows: scores, online softmax, O += P V.  Every K~ and
+// V fragment read from LDS feeds NB products.  Q~ carries the factor
+// log2(e)/sqrt(D), so scores are in log2 units.  m is the reference
+// maximum the running sum l and O are relative to.  The common step takes
+// P = exp2(S - m) with the reference as it stands and checks the sum of
+// each lane's P: at most 2^LAZY_LOG2 bounds every P, so all fit fp16 and
+// nothing else is needed (O and l share the reference, so any reference is
+// exact in the arithmetic).  A step that fails the check (a row's first
+// step, m = -inf, or a score far above the reference) recomputes its
+// scores and moves the reference to the row maximum, rescaling O and l.
+// MASK hides keys after klim[nb] (causal diagonal, ragged tail).
+constexpr float LAZY_LIMIT = 32768.f;   // 2^15: every P <= this fits fp16
 
-template <int D, int NB, bool MASK, int MB = 2>
-__device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l,
-                                         const half_t* Ks, const half_t* Vs,
-                                         const half8 (*qf)[D / 16], int k0, const int* klim,
-                                         int lane) {
-  const int l32 = lane & 31, g = lane >> 5;
-  f32x16 s[NB][MB];
-  float base[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) base[nb] = m[nb] == -INFINITY ? 0.f : m[nb];
+template <int D, int NB, int MB>
+__device__ __forceinline__ void fwd_scores(f32x16 (*s)[MB], const half_t* Ks,
+                                           const half8 (*qf)[D / 16], int l32, int g) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[nb][mb][r] = RA_FWD_SEED ? -base[nb] : 0.f;
-    }
+    for (int nb = 0; nb < NB; ++nb) s[nb][mb] = f32x16{};
     const half_t* row = Ks + sig(32 * mb + perm(l32)) * (D + 8) + 8 * g;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
@@ -91,39 +81,32 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
       for (int nb = 0; nb < NB; ++nb) s[nb][mb] = mfma(a, qf[nb][t], s[nb][mb]);
     }
   }
-  half8 pf[NB][2 * MB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float mx = -INFINITY;
+}
+
+template <int D, int NB, bool MASK, int MB = 2>
+__device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l,
+                                         const half_t* Ks, const half_t* Vs,
+                                         const half8 (*qf)[D / 16], int k0, const int* klim,
+                                         int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  f32x16 s[NB][MB];
+  fwd_scores<D, NB, MB>(s, Ks, qf, l32, g);
+  // scores minus the reference, masked keys at -inf
+  auto relative = [&](int nb, float ref) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = RA_FWD_SEED ? s[nb][mb][r] : s[nb][mb][r] - base[nb];
+        float x = s[nb][mb][r] - ref;
         if (MASK) {
           const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * g + (r & 7);
           x = key > klim[nb] ? -INFINITY : x;
         }
         s[nb][mb][r] = x;
-        mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool upd = (m[nb] == -INFINITY) ? (mx != -INFINITY) : (mx > RESCALE_SLACK);
-    if (__any(upd)) {  // rare: move the reference maximum
-      const float shift = upd ? mx : 0.f;
-      const float mn = upd ? base[nb] + mx : m[nb];
-      const float alpha = upd ? exp2_fast(m[nb] - mn) : 1.f;
-      l[nb] *= alpha;
-      m[nb] = mn;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) o[nb][cb] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][mb][r] -= shift;
-      }
-    }
+  };
+  auto exps = [&](int nb) {
     float ls = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -134,7 +117,49 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
         ls += pr;
       }
     }
-    l[nb] += ls;
+    return ls;
+  };
+  float ls[NB];
+  bool exact = false;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    relative(nb, m[nb]);
+    ls[nb] = exps(nb);
+    // NaN (m = -inf) fails the test too
+    exact |= m[nb] == -INFINITY || !(ls[nb] <= LAZY_LIMIT);
+  }
+  if (__any(exact)) {  // rare: the scores again, and the reference to the row maximum
+    fwd_scores<D, NB, MB>(s, Ks, qf, l32, g);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      relative(nb, 0.f);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][mb][r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // a row with no visible key yet keeps m = -inf (its P are 0)
+      const float mn = fmaxf(m[nb], mx);
+      const float alpha = m[nb] == -INFINITY ? 0.f : exp2_fast(m[nb] - mn);
+      l[nb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) o[nb][cb] *= alpha;
+      m[nb] = mn;
+      const float ref = mn == -INFINITY ? 0.f : mn;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][mb][r] -= ref;
+      }
+      ls[nb] = exps(nb);
+    }
+  }
+  half8 pf[NB][2 * MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    l[nb] += ls[nb];
     to_frags<MB>(s[nb], pf[nb]);
   }
   // O^T[c][q] += V^T[c][key] P^T[key][q]: V^T fragments by transposed reads
