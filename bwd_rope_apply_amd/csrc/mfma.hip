@@ -89,6 +89,9 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
                                          const half8 (*qf)[D / 16], int k0, const int* klim,
                                          int lane) {
   const int l32 = lane & 31, g = lane >> 5;
+  // the scheduler's LDS-read / MFMA interleaving strategy: more fragment
+  // reads stay ahead of the products
+  __builtin_amdgcn_iglp_opt(0);
   f32x16 s[NB][MB];
   fwd_scores<D, NB, MB>(s, Ks, qf, l32, g);
   // scores minus the reference, masked keys at -inf
@@ -224,6 +227,9 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
                                           const half_t* vrow, int r0, int key, int lane,
                                           half8* ds_out = nullptr, bool key_ok = true) {
   const int l32 = lane & 31, g = lane >> 5;
+  // the scheduler's LDS-read / MFMA interleaving strategy: about 8 fragment
+  // reads stay ahead of the products instead of 1-2
+  __builtin_amdgcn_iglp_opt(0);
   f32x16 s[NMB], dp[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
