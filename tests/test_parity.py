@@ -113,6 +113,13 @@ def test_bf16_growing_scores(causal):
     assert e_o <= BF16_TOL and e_lse <= BF16_TOL, (e_o, e_lse)
 
 
+def test_bf16_more_than_4096_heads():
+    """B = 41, H = 100 (4100 (b, h) pairs) at N = 160: the prep pass's grid
+    takes the heads past 4096 through its z dimension, and every kernel
+    indexes heads past it (the corner, the main kernels, the dS panels)."""
+    _check(W.make_inputs(W.get("long_8k", B=41, H=100, N=160, seed=4100)))
+
+
 # The backward with the smallest workspace: no dS panels, so dQ recomputes
 # the scores and dP instead of reading the dS that the dK/dV pass stored.
 RECOMPUTE_CASES = [("long_8k", 3, 700, True), ("layer_2k", 2, 129, True), ("layer_2k", 2, 1, True),
