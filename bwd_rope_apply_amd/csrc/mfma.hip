@@ -58,7 +58,7 @@ namespace {
 // log2(e)/sqrt(D), so scores are in log2 units.  m is the reference
 // maximum the running sum l and O are relative to.  The common step takes
 // P = exp2(S - m) with the reference as it stands and checks the sum of
-// each lane's P: at most 2^LAZY_LOG2 bounds every P, so all fit fp16 and
+// each lane's P: at most LAZY_LIMIT (2^15) bounds every P, so all fit fp16 and
 // nothing else is needed (O and l share the reference, so any reference is
 // exact in the arithmetic).  A step that fails the check (a row's first
 // step, m = -inf, or a score far above the reference) recomputes its
