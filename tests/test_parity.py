@@ -81,21 +81,22 @@ def test_bf16_noncausal(D):
     _check(W.make_inputs(wl), causal=False)
 
 
+@pytest.mark.parametrize("name", ["long_8k", "vlong_32k"])
 @pytest.mark.parametrize("causal", [True, False])
-def test_bf16_growing_scores(causal):
+def test_bf16_growing_scores(causal, name):
     """Key rows scaled by 2^(2.5 j / N) along the sequence, three of them
     3x more, and q scaled by 0.35 (log2-unit scores up to about 26).  Each
     row's largest scores come late, so the forward's softmax reference has
     to move mid-row.  Some steps have P sums past 2^15 and take the path
     that moves it to the row maximum.  Others keep single P between 2^8 and
     2^15 in fp16.  At N = 700 a CPU count of the reference moves found 17
-    and 100 such steps (causal).
+    and 100 such steps (long_8k, causal).
 
     Only the forward's outputs are held to the bar here.  At scores this
     large the backward's fp16 rounding of P and dS grows with the score
     (dQ reached 2.6e-2 of its RMS, causal), past the 2e-2 bar; its errors
-    are printed."""
-    wl = W.get("long_8k", B=1, H=2, N=700, seed=4242)
+    are printed.  long_8k's distributions at D = 128, vlong_32k's at D = 64."""
+    wl = W.get(name, B=1, H=2, N=700, seed=4242)
     inp = W.make_inputs(wl)
     f = 2.0 ** (2.5 * np.arange(wl.N) / wl.N)
     f[[300, 480, 610]] *= 3.0
