@@ -11,7 +11,7 @@ the stage bits and options of the ``_ex`` entry points as keywords),
 ``librope_attn.so``; build it with ``python -m bwd_rope_apply_amd.build``.
 ``workloads`` draws the seeded synthetic inputs.
 """
-from ._lib import fwd, bwd, load, workspace_bytes, RopeAttnError, FP32, BF16  # noqa: F401
+from ._lib import fwd, bwd, load, workspace_bytes, workspace_flags, RopeAttnError, FP32, BF16  # noqa: F401
 from ._lib import gram_select, gram_cascade  # noqa: F401
 
 rope_attn_fwd = fwd

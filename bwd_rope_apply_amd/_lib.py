@@ -103,6 +103,8 @@ def load() -> ctypes.CDLL:
     lib.rope_attn_fwd_ex.restype = i
     lib.rope_attn_bwd_ex.argtypes = [ctypes.c_uint, vp] + lib.rope_attn_bwd.argtypes
     lib.rope_attn_bwd_ex.restype = i
+    lib.rope_attn_workspace_flags.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_uint), vp]
+    lib.rope_attn_workspace_flags.restype = i
     lib.rope_attn_status_string.argtypes = [i]
     lib.rope_attn_status_string.restype = ctypes.c_char_p
     f = ctypes.c_float
@@ -157,11 +159,39 @@ def _shape(q, k, v):
     return tuple(int(x) for x in q.shape)
 
 
+def _same_device(name, t, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    """A caller-supplied tensor the library reads or writes: the given shape
+    and dtype, contiguous, on ``device`` (the kernels write exactly
+    prod(shape) elements of dtype through its pointer)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    _same_device(name, t, device)
+
+
+def _workspace(workspace, nbytes, device):
+    """The workspace tensor (any dtype, contiguous, on ``device``) and its
+    size in bytes; a new one of ``nbytes`` when None."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _same_device("workspace", workspace, device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _alpha(alpha, q, D):
     import torch
     if alpha is None:
         return None
-    if alpha.shape != (D // 2,) or alpha.dtype != torch.float32 or alpha.device != q.device:
+    if tuple(alpha.shape) != (D // 2,) or alpha.dtype != torch.float32 or alpha.device != q.device:
         raise ValueError("alpha must be a float32 [D/2] tensor on q's device")
     return alpha.contiguous()
 
@@ -190,13 +220,14 @@ def fwd(q, k, v, base: float, alpha=None, causal: bool = True, workspace=None,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+        _check_tensor("o", o, (B, H, N, D), torch.float32, q.device)
+        _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
     nbytes = workspace_bytes("fwd", B, H, N, D, dt, causal)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, wbytes = _workspace(workspace, nbytes, q.device)
     op = _opts(opts)
     st = lib.rope_attn_fwd_ex(stages, None if op is None else ctypes.addressof(op), _ptr(q), _ptr(k),
                               _ptr(v), _ptr(o), _ptr(lse), B, H, N, D, dt, float(base), _ptr(alpha),
-                              int(causal), _ptr(workspace), workspace.numel(), _stream(q.device))
+                              int(causal), _ptr(workspace), wbytes, _stream(q.device))
     _check("rope_attn_fwd", st)
     return o, lse
 
@@ -210,12 +241,9 @@ def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, works
     lib = load()
     B, H, N, D = _shape(q, k, v)
     dt = _dtype_code(q)
-    if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous():
-        raise ValueError("dO must match q in shape and dtype and be contiguous")
-    if o.shape != q.shape or o.dtype != torch.float32 or not o.is_contiguous():
-        raise ValueError("O must be a contiguous float32 [B,H,N,D] tensor")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("LSE must be a contiguous float32 [B,H,N] tensor")
+    _check_tensor("dO", do, (B, H, N, D), q.dtype, q.device)
+    _check_tensor("O", o, (B, H, N, D), torch.float32, q.device)
+    _check_tensor("LSE", lse, (B, H, N), torch.float32, q.device)
     alpha = _alpha(alpha, q, D)
     if out is None:
         dq = torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
@@ -224,16 +252,35 @@ def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, works
         da = torch.empty((D // 2,), dtype=torch.float32, device=q.device) if want_dalpha else None
     else:
         dq, dk, dv, da = out
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_tensor(name, t, (B, H, N, D), torch.float32, q.device)
+        if da is not None:
+            _check_tensor("dalpha", da, (D // 2,), torch.float32, q.device)
     nbytes = workspace_bytes("bwd", B, H, N, D, dt, causal)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, wbytes = _workspace(workspace, nbytes, q.device)
     op = _opts(opts)
     st = lib.rope_attn_bwd_ex(stages, None if op is None else ctypes.addressof(op), _ptr(q), _ptr(k),
                               _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                               _ptr(da), B, H, N, D, dt, float(base), _ptr(alpha), int(causal),
-                              _ptr(workspace), workspace.numel(), _stream(q.device))
+                              _ptr(workspace), wbytes, _stream(q.device))
     _check("rope_attn_bwd", st)
     return dq, dk, dv, da
+
+
+FLAG_FP16_RANGE = 1   # an entry of the scaled Q~, of K~ or of V exceeded fp16's range
+
+
+def workspace_flags(workspace) -> int:
+    """The range flags that the last PREP stage left in ``workspace`` (a
+    device tensor passed to fwd or bwd).  Synchronises the current stream."""
+    lib = load()
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    v = ctypes.c_uint(0)
+    st = lib.rope_attn_workspace_flags(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       ctypes.byref(v), _stream(workspace.device))
+    _check("rope_attn_workspace_flags", st)
+    return int(v.value)
 
 
 # ------------------------------------------------------------ token selection
@@ -268,11 +315,13 @@ def gram_select(x, tau: float, workspace=None, out=None, stages: int = GRAM_STAG
         cnt = torch.empty((B,), dtype=torch.int32, device=x.device)
     else:
         m, rep, cnt = out
+        _check_tensor("max_cos", m, (B, T), torch.float32, x.device)
+        _check_tensor("rep", rep, (B, T), torch.uint8, x.device)
+        _check_tensor("count", cnt, (B,), torch.int32, x.device)
     nbytes = int(lib.gram_select_workspace_bytes(B, T, d))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    workspace, wbytes = _workspace(workspace, nbytes, x.device)
     st = lib.gram_select_stages(stages, _ptr(xb), B, T, d, dt, float(tau), _ptr(m), _ptr(rep),
-                                _ptr(cnt), _ptr(workspace), workspace.numel(), _stream(x.device))
+                                _ptr(cnt), _ptr(workspace), wbytes, _stream(x.device))
     _check("gram_select", st)
     if x.dim() == 2:
         return m[0], rep[0], cnt
@@ -297,10 +346,14 @@ def gram_cascade(x, tau: float, prev, workspace=None, out=None):
         cnt = torch.empty((1,), dtype=torch.int32, device=x.device)
     else:
         m, rep, cnt = out
+        _check_tensor("max_cos", m, (T,), torch.float32, x.device)
+        _check_tensor("rep", rep, (T,), torch.uint8, x.device)
+        _check_tensor("count", cnt, (1,), torch.int32, x.device)
+    if prev.device != x.device:
+        raise ValueError("prev must be on x's device")
     nbytes = int(lib.gram_cascade_workspace_bytes(T, d))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    workspace, wbytes = _workspace(workspace, nbytes, x.device)
     st = lib.gram_cascade(_ptr(x), T, d, dt, float(tau), _ptr(prev), _ptr(m), _ptr(rep), _ptr(cnt),
-                          _ptr(workspace), workspace.numel(), _stream(x.device))
+                          _ptr(workspace), wbytes, _stream(x.device))
     _check("gram_cascade", st)
     return m, rep, cnt

@@ -91,10 +91,11 @@ int resolve(const rope_attn_options* o, const Shape& s, Opts& r) {
 // The dS panels come last, so the layouts with and without them agree on
 // every other region.
 struct Layout {
-  size_t theta, cs, qh, kh, vh, qlo, klo, bmask, doh, drow, rs, dkp, dvp, part, dsp;
+  size_t flags, theta, cs, qh, kh, vh, qlo, klo, bmask, amax, dsc, doh, drow, rs, dkp, dvp, part, dsp;
   int slots;
   size_t total() const {
-    return theta + cs + qh + kh + vh + qlo + klo + bmask + doh + drow + rs + dkp + dvp + part + dsp;
+    return flags + theta + cs + qh + kh + vh + qlo + klo + bmask + amax + dsc + doh + drow + rs +
+           dkp + dvp + part + dsp;
   }
 };
 
@@ -123,6 +124,7 @@ int mfma_slots(const Shape& s, bool panels) {
 Layout layout(Shape s, bool bwd, bool panels = false) {
   Layout L = {};
   s.blocks = 0;
+  L.flags = ALIGN;   // range flags: offset 0 of every layout
   L.theta = up(sizeof(double) * (s.D / 2));
   L.cs = up(sizeof(float2) * (size_t)s.N * (s.D / 2));
   // fp16 planes: every head's rows, then PLANE_PAD_ROWS zero rows
@@ -134,6 +136,10 @@ Layout layout(Shape s, bool bwd, bool panels = false) {
   }
   if (s.mask_ok()) L.bmask = up(sizeof(uint32_t) * s.bh() * n_blocks(s.N) * mask_words(s.N));
   if (bwd) {
+    if (s.bf16()) {
+      L.amax = up(sizeof(float) * s.bh() * AMAX_SLOTS);
+      L.dsc = up(sizeof(float) * s.bh());
+    }
     L.drow = up(sizeof(float) * s.bh() * s.N);
     if (s.bf16()) L.rs = up(sizeof(float) * s.bh() * rs_groups(s.N) * 64);
     if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * s.corner() * s.D);
@@ -173,10 +179,10 @@ int check_common(const Shape& s, double base, void* ws, size_t ws_bytes, bool bw
 }
 
 void tables(const Shape& s, const Opts& op, double base, const float* alpha, double* theta,
-            float2* cs, hipStream_t st) {
+            float2* cs, unsigned* flags, hipStream_t st) {
   TableParams t = {};
   t.cs = cs; t.theta_hat = theta; t.alpha = alpha; t.base = base; t.N = s.N; t.D = s.D;
-  t.rot = op.rot; t.pos0 = op.pos0;
+  t.rot = op.rot; t.pos0 = op.pos0; t.flags = flags;
   launch_table(t, st);
 }
 
@@ -242,6 +248,7 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const Layout L = layout(s, false);
   Carve c{reinterpret_cast<char*>(workspace)};
+  unsigned* flags = c.take<unsigned>(L.flags);
   double* theta = c.take<double>(L.theta);
   float2* cs = c.take<float2>(L.cs);
   half_t* qh = c.take<half_t>(L.qh);
@@ -252,11 +259,12 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   uint32_t* bmask = c.take<uint32_t>(L.bmask);
 
   if (stages & ROPE_ATTN_STAGE_PREP) {
-    tables(s, op, base, alpha, theta, cs, hs);
+    tables(s, op, base, alpha, theta, cs, flags, hs);
     if (op.bptr) block_mask(s, op, bmask, hs);
     if (s.bf16()) {
       PrepParams pp = {};
       pp.q = q; pp.k = k; pp.v = v; pp.cs = cs; pp.qh = qh; pp.kh = kh; pp.vh = vh;
+      pp.flags = flags;
       pp.qlo = qlo; pp.klo = klo; pp.rlo = s.corner();
       pp.bf16 = 1; pp.BH = (int)s.bh(); pp.N = N; pp.D = D;
       pp.qscale = LOG2E * op.scale;
@@ -325,6 +333,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   const bool panels = !op.bptr && Lp.dsp && workspace_bytes >= Lp.total();
   const Layout L = panels ? Lp : layout(s, true, false);
   Carve c{reinterpret_cast<char*>(workspace)};
+  unsigned* flags = c.take<unsigned>(L.flags);
   double* theta = c.take<double>(L.theta);
   float2* cs = c.take<float2>(L.cs);
   half_t* qh = c.take<half_t>(L.qh);
@@ -333,6 +342,8 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   half_t* qlo = c.take<half_t>(L.qlo);
   half_t* klo = c.take<half_t>(L.klo);
   uint32_t* bmask = c.take<uint32_t>(L.bmask);
+  float* amax = c.take<float>(L.amax);
+  float* dsc = c.take<float>(L.dsc);
   half_t* doh = c.take<half_t>(L.doh);
   float* drow = c.take<float>(L.drow);
   float* rs = c.take<float>(L.rs);
@@ -353,8 +364,13 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   if (stages & (ROPE_ATTN_STAGE_PREP | ROPE_ATTN_STAGE_PREP_GRAD)) {
     // PREP_GRAD alone: the table and the Q~, K~, V planes are the forward's
     const bool full = (stages & ROPE_ATTN_STAGE_PREP) != 0;
-    if (full) tables(s, op, base, alpha, theta, cs, hs);
+    if (full) tables(s, op, base, alpha, theta, cs, flags, hs);
     if (full && op.bptr) block_mask(s, op, bmask, hs);
+    if (s.bf16()) {  // per-head maxima of |dO| for its power-of-two scale
+      AbsmaxParams ap = {};
+      ap.x = dO; ap.amax = amax; ap.BH = BHi; ap.N = N; ap.D = D;
+      launch_absmax(ap, hs);
+    }
     PrepParams pp = {};
     pp.q = q; pp.k = k; pp.v = v; pp.dO = dO; pp.o = o; pp.cs = cs;
     pp.qh = full ? qh : nullptr; pp.kh = full ? kh : nullptr; pp.vh = full ? vh : nullptr;
@@ -363,8 +379,11 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
     pp.qlo = full ? qlo : nullptr; pp.klo = full ? klo : nullptr; pp.rlo = s.corner();
     pp.bf16 = s.bf16(); pp.BH = BHi; pp.N = N; pp.D = D;
     pp.qscale = LOG2E * op.scale;
+    pp.amax = amax; pp.dsc = dsc;
+    pp.flags = full ? flags : nullptr;
     launch_prep(pp, hs);
   }
+  mp.dsc = dsc;
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.qlo = qlo; mp.klo = klo; mp.q = q; mp.k = k;
   mp.cs = cs; mp.lse = lse; mp.drow = drow; mp.rs = rs; mp.dq = dq; mp.dk = dk; mp.dv = dv;
   set_blocks(mp, s, op, bmask);
@@ -420,6 +439,20 @@ int rope_attn_bwd_stages(unsigned stages, const void* q, const void* k, const vo
                          size_t workspace_bytes, void* stream) {
   return rope_attn_bwd_ex(stages, nullptr, q, k, v, o, dO, lse, dq, dk, dv, dalpha, B, H, N, D,
                           dtype, base, alpha, causal, workspace, workspace_bytes, stream);
+}
+
+int rope_attn_workspace_flags(const void* workspace, size_t workspace_bytes, unsigned* flags,
+                              void* stream) {
+  if (!workspace || !flags) return ROPE_ATTN_ERR_NULL;
+  if (misaligned(workspace)) return ROPE_ATTN_ERR_ALIGN;
+  if (workspace_bytes < sizeof(unsigned)) return ROPE_ATTN_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  unsigned v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(unsigned), hipMemcpyDeviceToHost, hs) != hipSuccess)
+    return ROPE_ATTN_ERR_HIP;
+  if (hipStreamSynchronize(hs) != hipSuccess) return ROPE_ATTN_ERR_HIP;
+  *flags = v;
+  return ROPE_ATTN_OK;
 }
 
 const char* rope_attn_status_string(int status) {

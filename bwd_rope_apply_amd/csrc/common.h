@@ -74,6 +74,22 @@ __host__ __device__ inline size_t panel_head(int N, int causal) {
 // is masked or multiplied by an exact zero, and all of them are finite.
 constexpr int PLANE_PAD_ROWS = 64;
 
+// Per-head power-of-two scaling of the upstream gradient (bf16 inputs).  The
+// backward is linear in dO, so each head's dO is multiplied by
+// s = 2^(2 - floor(log2 max|dO|)) before its fp16 conversion (its largest
+// entry lands in [4, 8)), D_i is taken from the scaled values, and 1 / s is
+// applied where dQ, dK and dV leave the accumulators.  Multiplying by a
+// power of two is exact, so gradients of any magnitude an fp32 or bf16
+// tensor holds keep fp16's full precision instead of falling into its
+// subnormals (below 6.1e-5) or overflowing it (above 65504).  The head's
+// maximum comes from AMAX_SLOTS partial maxima per head.
+constexpr int AMAX_SLOTS = 32;
+
+// Range flags (one word at the start of every workspace), set by the PREP
+// stage: an entry of the rotated, scaled Q~, of K~ or of V lay outside
+// fp16's finite range, so that operand became +-inf.
+constexpr unsigned FLAG_FP16_RANGE = 1u;
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -86,6 +102,13 @@ struct TableParams {
   int N, D;
   int rot;              // bands m < rot are rotated (partial RoPE), D/2 = all
   int pos0;             // position of row 0
+  unsigned* flags;      // range flags, cleared here (the first kernel of PREP), or null
+};
+
+struct AbsmaxParams {
+  const void* x;        // [BH][N][D] bf16
+  float* amax;          // [BH][AMAX_SLOTS] partial maxima of |x|
+  int BH, N, D;
 };
 
 struct PrepParams {
@@ -99,6 +122,9 @@ struct PrepParams {
   const float* lse;      // [B,H,N] forward LSE (natural log), with rs
   float* rs;             // [BH][rs_groups(N)][64] row scalars, or null
   float qscale;          // factor folded into the rotated Q plane
+  const float* amax;     // [BH][AMAX_SLOTS] partial maxima of |dO| (scales the dO plane), or null
+  float* dsc;            // [BH] written: 1 / (the head's dO scale), when amax is set
+  unsigned* flags;       // range flags (FLAG_FP16_RANGE), or null
   int bf16;              // input storage: 1 = bf16, 0 = fp32
   int BH, N, D;
 };
@@ -146,6 +172,7 @@ struct MfmaParams {
   float* dq; float* dk; float* dv;
   float* dk_part; float* dv_part;   // corner partials [BH][corner][D] or null
   half_t* dsp;                      // dS panels [BH][panel_head] (dK/dV writes, dQ reads), or null
+  const float* dsc;                 // [BH] 1 / (dO scale) of each head (backward), or null (1)
   float* dalpha_part;
   int slot0;
   const uint32_t* bmask;           // block visibility [BH][nb][W], or null (causal triangle / all)
@@ -167,6 +194,7 @@ struct DalphaParams {
 // ------------------------------------------------------------------ launchers
 void launch_table(const TableParams& p, hipStream_t s);
 void launch_prep(const PrepParams& p, hipStream_t s);
+void launch_absmax(const AbsmaxParams& p, hipStream_t s);
 void launch_block_mask(const BlockMaskParams& p, hipStream_t s);
 void launch_simt_fwd(const SimtParams& p, hipStream_t s);
 void launch_simt_dq(const SimtParams& p, hipStream_t s);
@@ -200,6 +228,9 @@ __device__ __forceinline__ void load4(const void* base, size_t idx, int bf16, fl
     x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
   }
 }
+
+// The factor that undoes a head's dO scaling in the backward epilogues.
+__device__ __forceinline__ float dscale_inv(const float* dsc, int bh) { return dsc ? dsc[bh] : 1.f; }
 
 // Whether key `key` is visible to query row `row` under a block mask (null:
 // all blocks visible; the causal mask is separate).

@@ -177,7 +177,7 @@ __device__ __forceinline__ void corner_dq(const MfmaParams& p, int bid) {
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
   if (row_ok)
-    finish_rows<D>(acc, p.scale, nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
+    finish_rows<D>(acc, p.scale * dscale_inv(p.dsc, bh), nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
                    head + (size_t)qrow * D, p.bf16, p.dq + head + (size_t)qrow * D, (float)qrow, wv,
                    g);
   store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
@@ -250,7 +250,8 @@ __device__ __forceinline__ void corner_dkdv(const MfmaParams& p, int bid) {
     accumulate_tr<D>(dk, Ql, sh, lane);
   }
   if (key < nlo) {
-    // Q~ carries log2(e)/sqrt(D): dK~ = ln 2 * (dS^T Q~')
+    // Q~ carries log2(e)/sqrt(D): dK~ = ln 2 * (dS^T Q~'); the dO scale is undone here
+    const float dinv = dscale_inv(p.dsc, bh), kf2 = LN2 * dinv;
     float* dkp = p.dk_part + ((size_t)bh * p.corner + key) * D;
     float* dvp = p.dv_part + ((size_t)bh * p.corner + key) * D;
 #pragma unroll
@@ -259,10 +260,11 @@ __device__ __forceinline__ void corner_dkdv(const MfmaParams& p, int bid) {
       for (int rq = 0; rq < 4; ++rq) {
         const int c = 32 * cb + 8 * rq + 4 * g;
         *reinterpret_cast<float4*>(dkp + c) =
-            make_float4(dk[cb][4 * rq] * LN2, dk[cb][4 * rq + 1] * LN2, dk[cb][4 * rq + 2] * LN2,
-                        dk[cb][4 * rq + 3] * LN2);
+            make_float4(dk[cb][4 * rq] * kf2, dk[cb][4 * rq + 1] * kf2, dk[cb][4 * rq + 2] * kf2,
+                        dk[cb][4 * rq + 3] * kf2);
         *reinterpret_cast<float4*>(dvp + c) =
-            make_float4(dv[cb][4 * rq], dv[cb][4 * rq + 1], dv[cb][4 * rq + 2], dv[cb][4 * rq + 3]);
+            make_float4(dv[cb][4 * rq] * dinv, dv[cb][4 * rq + 1] * dinv, dv[cb][4 * rq + 2] * dinv,
+                        dv[cb][4 * rq + 3] * dinv);
       }
     }
   }

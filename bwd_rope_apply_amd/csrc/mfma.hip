@@ -58,9 +58,10 @@ namespace {
 // log2(e)/sqrt(D), so scores are in log2 units.  m is the reference
 // maximum the running sum l and O are relative to.  The common step takes
 // P = exp2(S - m) with the reference as it stands and checks the sum of
-// each lane's P: at most LAZY_LIMIT (2^15) bounds every P, so all fit fp16 and
-// nothing else is needed (O and l share the reference, so any reference is
-// exact in the arithmetic).  A step that fails the check (a row's first
+// each lane's fp16 P: at most LAZY_LIMIT (2^15) bounds every P, so all fit
+// fp16 and nothing else is needed (O and l share the reference, so any
+// reference is exact in the arithmetic; a P past fp16's range makes the sum
+// +inf).  A step that fails the check (a row's first
 // step, m = -inf, or a score far above the reference) recomputes its
 // scores and moves the reference to the row maximum, rescaling O and l.
 // MASK hides keys after klim[nb] (causal diagonal, ragged tail).
@@ -110,25 +111,38 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
     }
   };
   auto exps = [&](int nb) {
-    float ls = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = exp2_fast(s[nb][mb][r]);
-        s[nb][mb][r] = pr;
-        ls += pr;
+      for (int r = 0; r < 16; ++r) s[nb][mb][r] = exp2_fast(s[nb][mb][r]);
+    }
+  };
+  // the step's fp16 weights, and their sum in fp32 (two interleaved chains of
+  // v_dot2 against (1, 1)): a weight past fp16's range makes the sum +inf
+  half8 pf[NB][2 * MB];
+  auto weights = [&](int nb) {
+    to_frags<MB>(s[nb], pf[nb]);
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2 * MB; ++t) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 4) {
+        a = __builtin_amdgcn_fdot2(half2v{pf[nb][t][e], pf[nb][t][e + 1]}, half2v{1.0f16, 1.0f16}, a,
+                                   false);
+        b = __builtin_amdgcn_fdot2(half2v{pf[nb][t][e + 2], pf[nb][t][e + 3]},
+                                   half2v{1.0f16, 1.0f16}, b, false);
       }
     }
-    return ls;
+    return a + b;
   };
   float ls[NB];
   bool exact = false;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     relative(nb, m[nb]);
-    ls[nb] = exps(nb);
-    // NaN (m = -inf) fails the test too
+    exps(nb);
+    ls[nb] = weights(nb);
+    // NaN (m = -inf) and +inf (a weight past fp16) fail the test too
     exact |= m[nb] == -INFINITY || !(ls[nb] <= LAZY_LIMIT);
   }
   if (__any(exact)) {  // rare: the scores again, and the reference to the row maximum
@@ -156,15 +170,15 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nb][mb][r] -= ref;
       }
-      ls[nb] = exps(nb);
+      exps(nb);
+      ls[nb] = weights(nb);
     }
   }
-  half8 pf[NB][2 * MB];
+  // l sums the fp16 weights that the PV product uses: it is O's normaliser
+  // (a row whose weight sits on one key then keeps that key's value, the
+  // weight's rounding cancelling) and the LSE's sum
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    l[nb] += ls[nb];
-    to_frags<MB>(s[nb], pf[nb]);
-  }
+  for (int nb = 0; nb < NB; ++nb) l[nb] += ls[nb];
   // O^T[c][q] += V^T[c][key] P^T[key][q]: V^T fragments by transposed reads
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) {
@@ -500,7 +514,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
   if (row_ok)
-    finish_rows<D>(acc, p.scale, nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
+    finish_rows<D>(acc, p.scale * dscale_inv(p.dsc, bh), nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
                    head + (size_t)qrow * D, p.bf16, p.dq + head + (size_t)qrow * D, (float)qrow, wv,
                    g);
   store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
@@ -655,8 +669,10 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     const bool has_part = p.dk_part && key < p.corner;
     const float* dkp = has_part ? p.dk_part + ((size_t)bh * p.corner + key) * D : nullptr;
     const float* dvp = has_part ? p.dv_part + ((size_t)bh * p.corner + key) * D : nullptr;
-    // Q~ carries log2(e)/sqrt(D): dK~ = dS^T Q~ / sqrt(D) = ln 2 * (dS^T Q~')
-    finish_rows<D>(dk, LN2, dkp, p.cs + (size_t)key * (D / 2), p.k, head + (size_t)key * D,
+    // Q~ carries log2(e)/sqrt(D): dK~ = dS^T Q~ / sqrt(D) = ln 2 * (dS^T Q~'); the
+    // dO scale is undone here (the corner partials are final already)
+    const float dinv = dscale_inv(p.dsc, bh);
+    finish_rows<D>(dk, LN2 * dinv, dkp, p.cs + (size_t)key * (D / 2), p.k, head + (size_t)key * D,
                    p.bf16, p.dk + head + (size_t)key * D, (float)key, wv, g);
     float* dvrow = p.dv + head + (size_t)key * D;
 #pragma unroll
@@ -664,7 +680,8 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int c = 32 * cb + 8 * rq + 4 * g;
-        float4 v = make_float4(dv[cb][4 * rq], dv[cb][4 * rq + 1], dv[cb][4 * rq + 2], dv[cb][4 * rq + 3]);
+        float4 v = make_float4(dv[cb][4 * rq] * dinv, dv[cb][4 * rq + 1] * dinv,
+                               dv[cb][4 * rq + 2] * dinv, dv[cb][4 * rq + 3] * dinv);
         if (dvp) {
           const float4 pr = *reinterpret_cast<const float4*>(dvp + c);
           v.x += pr.x; v.y += pr.y; v.z += pr.z; v.w += pr.w;
@@ -815,7 +832,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   for (int j = 0; j < 2; ++j) {
     const int qrow = wrow0 + 32 * j + l32;
     if (active && qrow >= p.corner && qrow < p.N) {
-      finish_rows<D>(acc[j], p.scale, nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
+      finish_rows<D>(acc[j], p.scale * dscale_inv(p.dsc, bh), nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
                      head + (size_t)qrow * D, p.bf16, p.dq + head + (size_t)qrow * D, (float)qrow,
                      wj, g);
 #pragma unroll

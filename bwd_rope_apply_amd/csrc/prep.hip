@@ -20,6 +20,7 @@ __global__ void table_kernel(TableParams p) {
   // gradient through the theta_hat factor
   const double th = m < p.rot ? exp(a) * pow(p.base, -2.0 * (double)m / (double)p.D) : 0.0;
   if (pos == 0) p.theta_hat[m] = th;
+  if (idx == 0 && p.flags) *p.flags = 0u;
   double s, c;
   sincos((double)(pos + p.pos0) * th, &s, &c);
   p.cs[idx] = make_float2((float)c, (float)s);
@@ -87,6 +88,52 @@ __device__ __forceinline__ void store8lo(half_t* dst, const float* x) {
   *reinterpret_cast<half8*>(dst) = h;
 }
 
+// Partial maxima of |dO| (bf16), AMAX_SLOTS per head: block (slot, bh)
+// takes every AMAX_SLOTS-th 256-chunk group of the head.  Grid (AMAX_SLOTS,
+// heads mod 4096, heads / 4096).
+__global__ __launch_bounds__(256) void absmax_kernel(AbsmaxParams p) {
+  __shared__ float red[4];
+  const int bh = (int)blockIdx.z * 4096 + (int)blockIdx.y;   // heads over y and z (y < 4096)
+  if (bh >= p.BH) return;
+  const size_t chunks = (size_t)p.N * p.D / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) +
+                                                    (size_t)bh * p.N * p.D);
+  uint32_t mx = 0;   // max of |x| as bf16 bit patterns (the order of non-negative floats)
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (size_t)AMAX_SLOTS * 256) {
+    const uint4 u = src[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mx = max(mx, w[i] & 0x7fffu);
+      mx = max(mx, (w[i] >> 16) & 0x7fffu);
+    }
+  }
+  float f = __uint_as_float(mx << 16);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) f = fmaxf(f, __shfl_xor(f, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = f;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    p.amax[(size_t)bh * AMAX_SLOTS + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+void launch_absmax(const AbsmaxParams& p, hipStream_t s) {
+  const dim3 grid(AMAX_SLOTS, (unsigned)(p.BH < 4096 ? p.BH : 4096), (unsigned)((p.BH + 4095) / 4096));
+  hipLaunchKernelGGL(absmax_kernel, grid, dim3(256), 0, s, p);
+}
+
+// The head's dO scale s = 2^(2 - floor(log2 max)), clamped to [2^-126, 2^126]
+// (1 for a head whose dO is all zero or not finite), from its partial maxima.
+__device__ __forceinline__ float dO_scale(const float* amax) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < AMAX_SLOTS; ++i) mx = fmaxf(mx, amax[i]);
+  if (!(mx > 0.f) || !(mx <= 3.0e38f)) return 1.f;
+  const int e = (int)((__float_as_uint(mx) >> 23) & 0xffu);   // biased exponent (0: subnormal)
+  const int sh = min(126, max(-126, 129 - max(e, 1)));        // 2 - (e - 127)
+  return __uint_as_float((uint32_t)(sh + 127) << 23);
+}
+
 // BF16: the input storage (compile time, so that no branch separates a
 // load from its use and every load of a thread issues before the first wait)
 // Grid: x over the chunks of one head (N * D / 8 < 2^28), y and z over the
@@ -105,6 +152,9 @@ __global__ void prep_kernel(PrepParams p) {
   const int chunk = lin & (cpr - 1);
   const size_t row = (size_t)bh * p.N + pos;      // bh * N + pos
   const size_t e0 = row * p.D + (size_t)chunk * 8;
+  // this head's dO scale (a power of two; 1 without amax)
+  const float dsc = (p.amax && bh < p.BH) ? dO_scale(p.amax + (size_t)bh * AMAX_SLOTS) : 1.f;
+  if (p.amax && p.dsc && lin == 0 && bh < p.BH) p.dsc[bh] = 1.f / dsc;
   float xq[8], xk[8], xv[8], xd[8];
   Raw8 rq = {}, rk = {}, rv = {}, rd = {};
   float4 oa = {}, ob = {};
@@ -137,7 +187,22 @@ __global__ void prep_kernel(PrepParams p) {
       rot(cs[i].x, cs[i].y, xk[2 * i], xk[2 * i + 1]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xq[i] *= p.qscale;
+    for (int i = 0; i < 8; ++i) {
+      xq[i] *= p.qscale;
+      xd[i] *= dsc;
+    }
+    if (p.flags) {
+      // an operand entry fp16 cannot hold (it would become +-inf)
+      bool out = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (p.qh) out |= !(fabsf(xq[i]) <= 65504.f);
+        if (p.kh) out |= !(fabsf(xk[i]) <= 65504.f);
+        if (p.vh) out |= !(fabsf(xv[i]) <= 65504.f);
+      }
+      if (__any(out) && (threadIdx.x & 63) == __builtin_amdgcn_readfirstlane(threadIdx.x & 63))
+        atomicOr(p.flags, FLAG_FP16_RANGE);
+    }
     if (p.qh) store8h(p.qh + e0, xq);
     if (p.kh) store8h(p.kh + e0, xk);
     if (p.vh) store8h(p.vh + e0, xv);

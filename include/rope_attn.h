@@ -50,8 +50,29 @@
  * 128 per started 8192 positions; one 128-row block with block lists), whose
  * products use split fp16 operands (hi + lo, three products per
  * contraction, about 22-bit operands) with float32 accumulation.  Calls with
- * fp32 inputs run in float32 throughout.  The fp16 operands require |Q|,
- * |K|, |V|, |dO| entries below 6.5e4.
+ * fp32 inputs run in float32 throughout.
+ *
+ * Input domain of the bf16 path (fp16 operands):
+ *  - dO: any finite magnitude.  The backward is linear in dO, so each head's
+ *    dO is scaled by a power of two (exact) that puts its largest entry in
+ *    [4, 8) before the fp16 conversion, and the scale is undone in dQ, dK,
+ *    dV and dalpha.  Gradients of 1e-30 or 1e30 get the same relative
+ *    accuracy as gradients of 1.
+ *  - Q, K, V: entries of the rotated Q~ * log2(e) * scale, of K~ and of V
+ *    must lie within fp16's finite range, |x| <= 65504 (for K and V about
+ *    |x| < 4.6e4, since the rotation mixes pairs).  The PREP stage sets
+ *    ROPE_ATTN_FLAG_FP16_RANGE in the workspace when an entry does not
+ *    (that operand became +-inf and the outputs are not meaningful); read it
+ *    with rope_attn_workspace_flags.  Entries below 6.1e-5 in magnitude keep
+ *    fp16's absolute precision (2^-24) but lose relative precision.
+ *  - accuracy: the error of each output row is a small fraction of that
+ *    row's own size (measured max |err_row| <= 1.3e-2 * rms(row), typically
+ *    2e-3 to 8e-3, for scores up to 26 in log2 units).  Normalised by the
+ *    whole tensor's RMS instead, the error grows with the tensor's
+ *    peak-to-RMS ratio max|x| / rms(x), so max |err| <= 2e-2 * rms(x) holds
+ *    for outputs whose largest entries are within ROPE_ATTN_PEAK_RATIO_MAX
+ *    times their RMS (typical workloads: 3 to 16); inputs with a few rows
+ *    far above the rest (gradient ratios of 30 to 60) reach 3e-2 there.
  *
  * bwd_rope_apply_amd/examples/rope_attn_example.cpp is a plain C++ caller of
  * these entry points (one problem from a file, forward and backward).
@@ -225,6 +246,22 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
                      float* dk, float* dv, float* dalpha, int B, int H, int N, int D, int dtype,
                      double base, const float* alpha, int causal, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Range flags that the PREP stage leaves at the start of the workspace
+ * (cleared by every PREP, kept by the other stages and by PREP_GRAD). */
+#define ROPE_ATTN_FLAG_FP16_RANGE 1u /* an entry of Q~ (scaled), K~ or V exceeded 65504 */
+
+/* The largest peak-to-RMS ratio of an output tensor (O, dQ, dK, dV) at
+ * which the bf16 path is specified to meet max |err| <= 2e-2 * rms. */
+#define ROPE_ATTN_PEAK_RATIO_MAX 20
+
+/* Copies the range flags of `workspace` (as the last PREP stage on it left
+ * them) into *flags on the host.  Enqueues a 4-byte device-to-host copy on
+ * `stream` and synchronises that stream, so it waits for every call enqueued
+ * before it.  Returns ROPE_ATTN_ERR_NULL, _ALIGN (workspace not 16-byte
+ * aligned), _WORKSPACE (workspace_bytes < 4) or _HIP on failure. */
+int rope_attn_workspace_flags(const void* workspace, size_t workspace_bytes, unsigned* flags,
+                              void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* rope_attn_status_string(int status);

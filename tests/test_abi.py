@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
                            "rope_attn_bwd_workspace_bytes", "rope_attn_bwd_workspace_bytes_min",
                            "rope_attn_fwd", "rope_attn_fwd_ex",
                            "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
-                           "rope_attn_status_string"]
+                           "rope_attn_status_string", "rope_attn_workspace_flags"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -219,3 +219,40 @@ def test_headers_compile_as_plain_c(tmp_path):
                         f"-I{os.path.join(ROOT, 'include')}", "-c", str(src), "-o", str(tmp_path / "use.o")],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_workspace_flags_validation(lib):
+    """The range-flag query rejects a NULL, misaligned or too small workspace
+    and a NULL result pointer before any HIP call."""
+    v = ctypes.c_uint(7)
+    assert lib.rope_attn_workspace_flags(None, 1 << 20, ctypes.byref(v), None) == -1
+    assert lib.rope_attn_workspace_flags(A, 1 << 20, None, None) == -1
+    assert lib.rope_attn_workspace_flags(A + 4, 1 << 20, ctypes.byref(v), None) == -4
+    assert lib.rope_attn_workspace_flags(A, 2, ctypes.byref(v), None) == -5
+    assert v.value == 7
+
+
+def test_binding_checks_caller_tensors():
+    """The binding rejects caller-supplied tensors of the wrong shape, dtype,
+    layout or device before anything reaches the library (CPU tensors here:
+    each check is hit in order, the device check last)."""
+    import torch
+    from bwd_rope_apply_amd import _lib
+    dev = torch.device("cuda", 0)
+    ok = torch.zeros(2, 3, dtype=torch.float32)
+    cases = [
+        (torch.zeros(2, 4), "shape"),
+        (torch.zeros(2, 3, dtype=torch.bfloat16), "float32"),
+        (torch.zeros(3, 2).t(), "not contiguous"),
+        (ok, "device tensor"),
+    ]
+    for t, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            _lib._check_tensor("out", t, (2, 3), torch.float32, dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        _lib._workspace(torch.zeros(8, 2, dtype=torch.uint8).t(), 16, dev)
+    with pytest.raises(ValueError, match="device tensor"):
+        _lib._workspace(torch.zeros(16, dtype=torch.uint8), 16, dev)
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        _lib.fwd(q, q, q, 1e4)
