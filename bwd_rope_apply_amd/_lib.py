@@ -103,6 +103,8 @@ def load() -> ctypes.CDLL:
     lib.rope_attn_fwd_ex.restype = i
     lib.rope_attn_bwd_ex.argtypes = [ctypes.c_uint, vp] + lib.rope_attn_bwd.argtypes
     lib.rope_attn_bwd_ex.restype = i
+    lib.rope_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, vp, i, vp]
+    lib.rope_attn_fwd_noalloc.restype = i
     lib.rope_attn_workspace_flags.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_uint), vp]
     lib.rope_attn_workspace_flags.restype = i
     lib.rope_attn_status_string.argtypes = [i]
@@ -265,6 +267,28 @@ def bwd(q, k, v, o, do, lse, base: float, alpha=None, causal: bool = True, works
                               _ptr(workspace), wbytes, _stream(q.device))
     _check("rope_attn_bwd", st)
     return dq, dk, dv, da
+
+
+def fwd_noalloc(q, k, v, base: float, alpha=None, causal: bool = True, out: Optional[Tuple] = None):
+    """The forward through rope_attn_fwd_noalloc: the library's own fixed
+    device array is the workspace (no workspace argument).  ``out`` (o, lse)
+    as for fwd; the binding allocates them with torch only when not given."""
+    import torch
+    lib = load()
+    B, H, N, D = _shape(q, k, v)
+    dt = _dtype_code(q)
+    alpha = _alpha(alpha, q, D)
+    if out is None:
+        o = torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _check_tensor("o", o, (B, H, N, D), torch.float32, q.device)
+        _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
+    st = lib.rope_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D, dt,
+                                   float(base), _ptr(alpha), int(causal), _stream(q.device))
+    _check("rope_attn_fwd_noalloc", st)
+    return o, lse
 
 
 FLAG_FP16_RANGE = 1   # an entry of the scaled Q~, of K~ or of V exceeded fp16's range

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librope_attn.so")
 EXAMPLE = os.path.join(HERE, "rope_attn_example")
-SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "corner.hip", "gram.hip"]
+SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "corner.hip", "gram.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

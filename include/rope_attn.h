@@ -263,6 +263,25 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
 int rope_attn_workspace_flags(const void* workspace, size_t workspace_bytes, unsigned* flags,
                               void* stream);
 
+/* The forward (rope_attn_fwd) for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Its workspace is a file-scope
+ * device array of ROPE_ATTN_NOALLOC_SCRATCH_BYTES held by every GPU the
+ * library runs on until the process ends; the call allocates nothing and
+ * looks up this GPU's copy of the array once (on the first call on the
+ * device).  Arguments, outputs and results are exactly rope_attn_fwd's.
+ * Returns ROPE_ATTN_ERR_WORKSPACE when the problem needs more than the array
+ * holds (rope_attn_fwd_workspace_bytes > ROPE_ATTN_NOALLOC_SCRATCH_BYTES, for
+ * example B*H*N*D above about 1e7 at N = 2048), ROPE_ATTN_ERR_HIP when the
+ * array's address cannot be obtained, and rope_attn_fwd's other statuses.
+ * Calls on one GPU share its array: calls that overlap in time on one GPU
+ * (on different streams, or from several threads without ordering) race and
+ * give wrong results; calls ordered on one stream are safe. */
+#define ROPE_ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int rope_attn_fwd_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                          int H, int N, int D, int dtype, double base, const float* alpha,
+                          int causal, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* rope_attn_status_string(int status);
 

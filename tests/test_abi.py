@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
                            "gram_select_stages", "gram_select_workspace_bytes",
                            "rope_attn_bwd", "rope_attn_bwd_ex", "rope_attn_bwd_stages",
                            "rope_attn_bwd_workspace_bytes", "rope_attn_bwd_workspace_bytes_min",
-                           "rope_attn_fwd", "rope_attn_fwd_ex",
+                           "rope_attn_fwd", "rope_attn_fwd_ex", "rope_attn_fwd_noalloc",
                            "rope_attn_fwd_stages", "rope_attn_fwd_workspace_bytes",
                            "rope_attn_status_string", "rope_attn_workspace_flags"]
 
@@ -256,3 +256,13 @@ def test_binding_checks_caller_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         _lib.fwd(q, q, q, 1e4)
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation forward validates like the forward and rejects a
+    problem larger than its fixed array before any HIP call."""
+    assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 1, 16, 96, 1, 1e4, None, 1, None) == -2
+    assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 1, 16, 64, 9, 1e4, None, 1, None) == -3
+    assert lib.rope_attn_fwd_noalloc(None, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, None) == -1
+    # 1 x 64 x 8192 x 128 bf16 needs ~390 MiB of workspace, past the 64 MiB array
+    assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 64, 8192, 128, 1, 1e4, None, 1, None) == -5
