@@ -140,3 +140,21 @@ def test_readings():
     rms = np.sqrt(np.mean(ref ** 2))
     assert E.reading_a(got, ref) == pytest.approx(1.0 / rms)
     assert E.reading_b(got, ref) == pytest.approx(0.1)
+
+
+def test_floor_table_design_choice():
+    """The committed table generator on layer_2k (two full-length heads): the
+    design's rounding points (fp16 operands and the split-fp16 corner) stay
+    under the 2e-2 bar on every tensor under reading A, while bf16 operands
+    do not; without the corner the early rows raise reading A while reading
+    B (per row) does not move."""
+    from oracle import floor_table as F
+    rows = {v: fl for _, v, _, fl in F.table(["layer_2k"], heads=2, workers=4)}
+    design, nocorner, bf = (rows[v] for v, _, _ in F.VARIANTS)
+    for n in F.NAMES:
+        assert design[n][0] < 2e-2 and design[n][1] < 2e-2, (n, design[n])
+        assert nocorner[n][0] > design[n][0], n
+        assert abs(nocorner[n][1] - design[n][1]) < 1e-3, n
+    assert max(bf[n][0] for n in F.NAMES) > 2e-2
+    assert "| layer_2k | fp16 + corner (design) | 128 |" in F.markdown(
+        [("layer_2k", v, 128, rows[v]) for v, _, _ in F.VARIANTS])
