@@ -138,6 +138,38 @@ def device_info():
             "peak_fp16_tflops_at_2p4ghz": round(cus * 4 * 1024 * 2.4e9 / 1e12, 1)}
 
 
+def clock_sample(run_kernel, wall_ms: float = 0.8):
+    """Shader clock (GHz) of one CU: a one-wave probe kernel counts shader
+    cycles over a fixed wall-clock interval.  ``run_kernel`` (or None for an
+    idle GPU) is launched on the current stream right after the probe is
+    queued on a second stream (default priority), so the interval overlaps
+    that kernel.  Returns None if the probe library is missing."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "bwd_rope_apply_amd", "libra_clock.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.ra_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+    lib.ra_clock_probe.restype = ctypes.c_int
+    khz = int(lib.ra_wall_clock_khz())
+    if khz <= 0:
+        return None
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    ticks = int(wall_ms * khz)
+    if lib.ra_clock_probe(out.data_ptr(), ticks, side.cuda_stream) != 0:
+        return None
+    if run_kernel is not None:
+        run_kernel()
+    torch.cuda.synchronize()
+    cycles, wall = (int(x) for x in out.cpu().tolist())
+    if wall <= 0:
+        return None
+    return cycles / (wall / (khz * 1e3)) / 1e9
+
+
 def cpu_baseline(inp, wl):
     """The float64 oracle on one head of the same inputs (a bounded sample),
     timed on the host cores, scaled to TFLOP/s with the same flop count."""
@@ -402,6 +434,17 @@ def main():
     stage_ms = {n: float(np.mean([evd[s][i].elapsed_time(evd[s][i + 1]) for s in range(nd)]))
                 for i, n in enumerate(names)}
     ms_step = wall * 1e3 / args.steps
+    # shader clock of a CU while the dominant kernel runs, and idle
+    clocks = None
+    if wl.dtype == "bf16":
+        dom_bit = dict(BWD_CALLS)[DOMINANT[0]]
+        run_dom = lambda: _lib.bwd(q, k, v, o, do, lse, wl.base, alpha, wl.causal, workspace=ws_b,
+                                   out=(dq, dk, dv, da), stages=dom_bit, opts=opts)
+        under = [clock_sample(run_dom) for _ in range(3)]
+        idle = clock_sample(None)
+        if all(c is not None for c in under) and idle is not None:
+            clocks = {"sclk_ghz_under_" + DOMINANT[1]: round(float(np.median(under)), 3),
+                      "sclk_ghz_idle": round(idle, 3)}
     unit = 2.0 * pairs * D
     flops = 6.0 * unit
     value = flops / (ms_step * 1e-3) / 1e12
@@ -413,6 +456,12 @@ def main():
         roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                     "traffic": traffic, "avg_ms": round(call_ms[dom], 4)}
+        if clocks:
+            # the same peak at the clock the kernel actually ran at
+            ghz = clocks["sclk_ghz_under_" + kernel]
+            roofline["observed_sclk_ghz"] = ghz
+            roofline["peak_at_observed_sclk"] = round(PEAK_TFLOPS * ghz / 2.4, 1)
+            roofline["frac_at_observed_sclk"] = round(achieved / (PEAK_TFLOPS * ghz / 2.4), 4)
         dq_pass = ("recompute" if args.min_workspace or args.retrieved >= 0
                    or _lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal)
                    == _lib.workspace_bytes("bwd_min", B, H, N, D, dt_code, wl.causal) else "ds_panels")
@@ -451,7 +500,7 @@ def main():
         "tflops_fwd": round(2.0 * unit / (float(np.median(fwd_ev)) * 1e-3) / 1e12, 2),
         "tflops_bwd": round(4.0 * unit / (float(np.median(bwd_ev)) * 1e-3) / 1e12, 2),
         "tflops_fa_convention": round(7.0 * unit / (ms_step * 1e-3) / 1e12, 2),
-        "device": device_info(),
+        "device": dict(device_info(), **(clocks or {})),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, wl)

@@ -19,6 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librope_attn.so")
 EXAMPLE = os.path.join(HERE, "rope_attn_example")
+CLOCK_LIB = os.path.join(HERE, "libra_clock.so")
 SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "corner.hip", "gram.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
@@ -57,6 +58,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"example build failed:\n{r.stderr}")
     os.replace(EXAMPLE + ".tmp", EXAMPLE)
+    # the benchmark's shader-clock probe, a library of its own
+    obj = _compile("clockprobe.hip")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", CLOCK_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"clock probe link failed:\n{r.stderr}")
+    os.replace(CLOCK_LIB + ".tmp", CLOCK_LIB)
     if verbose:
         print(f"built {LIB} and {EXAMPLE}")
     return LIB

@@ -91,11 +91,11 @@ int resolve(const rope_attn_options* o, const Shape& s, Opts& r) {
 // The dS panels come last, so the layouts with and without them agree on
 // every other region.
 struct Layout {
-  size_t flags, theta, cs, qh, kh, vh, qlo, klo, bmask, amax, dsc, doh, drow, rs, dkp, dvp, part, dsp;
+  size_t flags, theta, cs, qh, kh, vh, qlo, klo, bmask, amax, dsc, doh, drow, rs, part, dsp;
   int slots;
   size_t total() const {
     return flags + theta + cs + qh + kh + vh + qlo + klo + bmask + amax + dsc + doh + drow + rs +
-           dkp + dvp + part + dsp;
+           part + dsp;
   }
 };
 
@@ -114,7 +114,7 @@ MfmaParams mfma_base(const Shape& s, float scale) {
 int mfma_slots(const Shape& s, bool panels) {
   MfmaParams m = mfma_base(s, 1.0f);
   if (panels) m.dsp = reinterpret_cast<half_t*>(ALIGN);  // only selects the dQ kernel's grid
-  return (s.corner() ? corner_dq_slots(m) : 0) + dq_mfma_slots(m) + dkdv_mfma_slots(m);
+  return dq_mfma_slots(m) + dkdv_mfma_slots(m);   // the corner's slots are the dQ launch's
 }
 
 // Region sizes do not depend on whether a call passes block lists (the
@@ -142,7 +142,6 @@ Layout layout(Shape s, bool bwd, bool panels = false) {
     }
     L.drow = up(sizeof(float) * s.bh() * s.N);
     if (s.bf16()) L.rs = up(sizeof(float) * s.bh() * rs_groups(s.N) * 64);
-    if (s.corner()) L.dkp = L.dvp = up(sizeof(float) * s.bh() * s.corner() * s.D);
     if (s.bf16()) {
       Shape sb = s;
       sb.blocks = 1;
@@ -347,16 +346,15 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   half_t* doh = c.take<half_t>(L.doh);
   float* drow = c.take<float>(L.drow);
   float* rs = c.take<float>(L.rs);
-  float* dkp = c.take<float>(L.dkp);
-  float* dvp = c.take<float>(L.dvp);
   float* part = c.take<float>(L.part);
   half_t* dsp = c.take<half_t>(L.dsp);
 
-  // d alpha partial slots: [exact or corner dQ rows | exact dK rows | MFMA dQ | MFMA dK]
+  // d alpha partial slots: [exact dQ rows | exact dK rows | dQ launch | dK/dV launch]; the
+  // dQ launch of the bf16 path also runs the corner (its dQ rows, and its share of dK, dV)
   const int BHi = (int)s.bh();
   MfmaParams mp = mfma_base(s, op.scale);
   mp.dsp = dsp;
-  const int n_exact_dq = s.bf16() ? (s.corner() ? corner_dq_slots(mp) : 0) : simt_slots(BHi, N);
+  const int n_exact_dq = s.bf16() ? 0 : simt_slots(BHi, N);
   const int n_exact_dk = s.bf16() ? 0 : simt_slots(BHi, N);
   const int n_dq = s.bf16() ? dq_mfma_slots(mp) : 0;
   const int n_dk = s.bf16() ? dkdv_mfma_slots(mp) : 0;
@@ -387,7 +385,7 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
   mp.qh = qh; mp.kh = kh; mp.vh = vh; mp.doh = doh; mp.qlo = qlo; mp.klo = klo; mp.q = q; mp.k = k;
   mp.cs = cs; mp.lse = lse; mp.drow = drow; mp.rs = rs; mp.dq = dq; mp.dk = dk; mp.dv = dv;
   set_blocks(mp, s, op, bmask);
-  mp.dk_part = dkp; mp.dv_part = dvp; mp.dalpha_part = part;
+  mp.dalpha_part = part;
   if (stages & ROPE_ATTN_STAGE_EXACT) {
     if (!s.bf16()) {
       SimtParams sp = {};
@@ -401,10 +399,8 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       launch_simt_dq(sp, hs);
       sp.slot0 = n_exact_dq;
       launch_simt_dkdv(sp, hs);
-    } else if (s.corner()) {
-      mp.slot0 = 0;
-      launch_corner_bwd(mp, hs);  // dK/dV as rotated-frame partials, no d alpha slots
     }
+    // bf16: the corner runs in the dQ launch (DQ stage)
   }
   // dK/dV first: with panels it writes the dS that the dQ product reads
   if ((stages & ROPE_ATTN_STAGE_DKDV) && s.bf16()) {

@@ -170,7 +170,6 @@ struct MfmaParams {
   const float* rs;                     // [BH][rs_groups(N)][64] row scalars (dK/dV)
   float* o; float* out_lse;
   float* dq; float* dk; float* dv;
-  float* dk_part; float* dv_part;   // corner partials [BH][corner][D] or null
   half_t* dsp;                      // dS panels [BH][panel_head] (dK/dV writes, dQ reads), or null
   const float* dsc;                 // [BH] 1 / (dO scale) of each head (backward), or null (1)
   float* dalpha_part;
@@ -179,7 +178,8 @@ struct MfmaParams {
   int nb, W;
   int bf16;
   int B, H, N, D;
-  int corner;      // rows [0, corner) are done by the corner kernels
+  int corner;      // rows [0, corner) are done by the corner's split-operand workgroups
+  int corner_at;   // dQ launch: grid position of its corner workgroups (set by the launcher)
   int causal;
   float scale;
 };
@@ -206,8 +206,6 @@ void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);
 int dq_mfma_slots(const MfmaParams& p);   // either dQ kernel (p.dsp selects)
 int dkdv_mfma_slots(const MfmaParams& p);
 void launch_corner_fwd(const MfmaParams& p, hipStream_t s);
-void launch_corner_bwd(const MfmaParams& p, hipStream_t s);   // dQ rows and dK/dV partials
-int corner_dq_slots(const MfmaParams& p);
 void launch_dalpha_reduce(const DalphaParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ device helpers

@@ -12,7 +12,7 @@
 // almost-linear time", Methodology 1 and 2): the normalised softmax s(x),
 // the weighted sum with V, beta = dO V^T, gamma = diag(s) beta - s s^T beta
 // = P o (dP - D), and the gradient back through the scores.
-#include "tile.h"
+#include "corner.h"
 
 namespace ra {
 
@@ -426,19 +426,29 @@ template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_kernel(MfmaParams p) {
   constexpr int SB = RA_DQ_BN, NMB = SB / 32, KB = SB * RA_DQ_SUB;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, KB>::ALLOC;
-  __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
-  __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
+  constexpr size_t MAIN = 4 * (size_t)TILE * sizeof(half_t);
+  // the main tiles, or a corner workgroup's tiles (the launch's first ones)
+  __shared__ __attribute__((aligned(16))) char pool[MAIN > corner_bwd_smem(D) ? MAIN : corner_bwd_smem(D)];
   __shared__ short blist[BL ? MAX_BLOCKS : 1];
   __shared__ int bcount;
   __shared__ float red[4 * (D / 2)];
+  const int ncorner = p.corner ? 3 * corner_blocks(p) : 0;
+  const int bx = (int)blockIdx.x;
+  if (bx >= p.corner_at && bx < p.corner_at + ncorner) {
+    corner_bwd<D>(p, bx - p.corner_at, pool);
+    return;
+  }
+  const int mb = bx < p.corner_at ? bx : bx - ncorner;   // this workgroup's dQ tile
+  half_t* Ks = reinterpret_cast<half_t*>(pool);
+  half_t* Vs = Ks + 2 * TILE;
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int ntiles = (p.N + BM - 1) / BM, t0 = p.corner / BM;
   int bh, t;
-  map_block(blockIdx.x, BH, ntiles - t0, true, bh, t);
-  const int slot = p.slot0 + blockIdx.x;
+  map_block(mb, BH, ntiles - t0, true, bh, t);
+  const int slot = p.slot0 + ncorner + mb;
   t += t0;
   const int q0 = t * BM, wrow0 = q0 + 32 * w, qrow = wrow0 + l32;
   const size_t head = (size_t)bh * p.N * D;
@@ -666,13 +676,11 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
   if (key < p.N) {
-    const bool has_part = p.dk_part && key < p.corner;
-    const float* dkp = has_part ? p.dk_part + ((size_t)bh * p.corner + key) * D : nullptr;
-    const float* dvp = has_part ? p.dv_part + ((size_t)bh * p.corner + key) * D : nullptr;
     // Q~ carries log2(e)/sqrt(D): dK~ = dS^T Q~ / sqrt(D) = ln 2 * (dS^T Q~'); the
-    // dO scale is undone here (the corner partials are final already)
+    // dO scale is undone here.  Keys below the corner get the corner's share
+    // (queries below it) added by the dQ launch.
     const float dinv = dscale_inv(p.dsc, bh);
-    finish_rows<D>(dk, LN2 * dinv, dkp, p.cs + (size_t)key * (D / 2), p.k, head + (size_t)key * D,
+    finish_rows<D>(dk, LN2 * dinv, nullptr, p.cs + (size_t)key * (D / 2), p.k, head + (size_t)key * D,
                    p.bf16, p.dk + head + (size_t)key * D, (float)key, wv, g);
     float* dvrow = p.dv + head + (size_t)key * D;
 #pragma unroll
@@ -680,13 +688,9 @@ __global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int c = 32 * cb + 8 * rq + 4 * g;
-        float4 v = make_float4(dv[cb][4 * rq] * dinv, dv[cb][4 * rq + 1] * dinv,
-                               dv[cb][4 * rq + 2] * dinv, dv[cb][4 * rq + 3] * dinv);
-        if (dvp) {
-          const float4 pr = *reinterpret_cast<const float4*>(dvp + c);
-          v.x += pr.x; v.y += pr.y; v.z += pr.z; v.w += pr.w;
-        }
-        *reinterpret_cast<float4*>(dvrow + c) = v;
+        *reinterpret_cast<float4*>(dvrow + c) =
+            make_float4(dv[cb][4 * rq] * dinv, dv[cb][4 * rq + 1] * dinv,
+                        dv[cb][4 * rq + 2] * dinv, dv[cb][4 * rq + 3] * dinv);
       }
     }
   }
@@ -729,17 +733,27 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   constexpr int CB = D / 32, TK = TileDMA<D, DQP_KB>::ALLOC, TS = DQP_TS;
   constexpr int NS = DQP_STAGES;
   static_assert(TS * 2 == 16 * 1024, "four 1 KiB copies per wave per panel tile");
-  __shared__ __attribute__((aligned(16))) half_t Ks[NS * TK];
-  __shared__ __attribute__((aligned(16))) half_t Ss[NS * TS];
+  constexpr size_t MAIN = (size_t)NS * (TK + TS) * sizeof(half_t);
+  // the ring, or a corner workgroup's tiles (the launch's first ones)
+  __shared__ __attribute__((aligned(16))) char pool[MAIN > corner_bwd_smem(D) ? MAIN : corner_bwd_smem(D)];
   __shared__ float red[4 * (D / 2)];
+  const int ncorner = p.corner ? 3 * corner_blocks(p) : 0;
+  const int bx = (int)blockIdx.x;
+  if (bx >= p.corner_at && bx < p.corner_at + ncorner) {
+    corner_bwd<D>(p, bx - p.corner_at, pool);
+    return;
+  }
+  const int mb = bx < p.corner_at ? bx : bx - ncorner;   // this workgroup's panel
+  half_t* Ks = reinterpret_cast<half_t*>(pool);
+  half_t* Ss = Ks + NS * TK;
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int np = n_panels(p.N), t0 = p.corner / PANEL;
   int bh, t;
-  map_block(blockIdx.x, BH, np - t0, true, bh, t);
-  const int slot = p.slot0 + blockIdx.x;
+  map_block(mb, BH, np - t0, true, bh, t);
+  const int slot = p.slot0 + ncorner + mb;
   t += t0;
   const int q0 = t * PANEL, wrow0 = q0 + 64 * w;
   const size_t head = (size_t)bh * p.N * D;
@@ -854,7 +868,12 @@ int dq_panel_blocks(const MfmaParams& p) {  // panels past the corner
 
 }  // namespace
 
-int dq_mfma_slots(const MfmaParams& p) { return p.dsp ? dq_panel_blocks(p) : fwd_blocks(p); }
+// dQ launch: the corner workgroups (dQ rows and dK, dV shares below the
+// corner) first, then the dQ product's
+int dq_corner_blocks(const MfmaParams& p) { return p.corner ? 3 * corner_blocks(p) : 0; }
+int dq_mfma_slots(const MfmaParams& p) {
+  return dq_corner_blocks(p) + (p.dsp ? dq_panel_blocks(p) : fwd_blocks(p));
+}
 int dkdv_mfma_slots(const MfmaParams& p) { return dkdv_blocks(p); }
 
 #define RA_LAUNCH1(KERNEL, ...)                                                                 \
@@ -878,16 +897,25 @@ void launch_fwd_mfma(const MfmaParams& p, hipStream_t s) {
   const int nb = p.B * p.H * max(0, (p.N + FWD_BM - 1) / FWD_BM - p.corner / FWD_BM);
   if (nb > 0) RA_LAUNCH(fwd_kernel, nb);
 }
-void launch_dq_mfma(const MfmaParams& p, hipStream_t s) {
+// The corner workgroups (latency-bound chains of a few to a few tens of
+// steps) come last in the dQ launch's grid: the grid issues the heaviest dQ
+// tiles first, and corner workgroups at its front would hold those back and
+// lengthen the launch; at its end they run beside the lightest tiles
+// (measured: at the front +22 us, in the middle +11 us, at the end +0 at
+// 1 x 32 x 8192 x 128).
+void launch_dq_mfma(const MfmaParams& p_in, hipStream_t s) {
+  MfmaParams p = p_in;
   if (p.dsp) {  // dense attention with the dS panels written by the dK/dV pass (D = 128)
-    const int nb = dq_panel_blocks(p);
+    p.corner_at = dq_panel_blocks(p);
+    const int nb = dq_corner_blocks(p) + dq_panel_blocks(p);
     const dim3 grid((unsigned)nb), block(256);
     if (nb <= 0) return;
     if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((dq_panel_kernel<128, false>), grid, block, 0, s, p);
     return;
   }
-  const int nb = fwd_blocks(p);
+  p.corner_at = fwd_blocks(p);
+  const int nb = dq_corner_blocks(p) + fwd_blocks(p);
   if (nb > 0) RA_LAUNCH(dq_kernel, nb);
 }
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s) {

@@ -99,13 +99,23 @@ __global__ __launch_bounds__(256) void absmax_kernel(AbsmaxParams p) {
   const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) +
                                                     (size_t)bh * p.N * p.D);
   uint32_t mx = 0;   // max of |x| as bf16 bit patterns (the order of non-negative floats)
-  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (size_t)AMAX_SLOTS * 256) {
-    const uint4 u = src[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  constexpr size_t STRIDE = (size_t)AMAX_SLOTS * 256;
+  constexpr int U = 4;   // loads in flight per thread
+  for (size_t c0 = (size_t)blockIdx.x * 256 + threadIdx.x; c0 < chunks; c0 += STRIDE * U) {
+    uint4 u[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mx = max(mx, w[i] & 0x7fffu);
-      mx = max(mx, (w[i] >> 16) & 0x7fffu);
+    for (int j = 0; j < U; ++j) {
+      const size_t c = c0 + STRIDE * j;
+      u[j] = c < chunks ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mx = max(mx, w[i] & 0x7fffu);
+        mx = max(mx, (w[i] >> 16) & 0x7fffu);
+      }
     }
   }
   float f = __uint_as_float(mx << 16);
@@ -293,9 +303,24 @@ __global__ void dalpha_kernel(DalphaParams p) {
   const int m = blockIdx.x;
   const int half = p.D / 2;
   __shared__ double red[256];
-  double acc = 0.0;
-  for (int s = threadIdx.x; s < p.slots; s += 256) acc += (double)p.part[(size_t)s * half + m];
-  red[threadIdx.x] = acc;
+  // eight independent partial sums per thread, so its loads are all in
+  // flight at once; they combine in a fixed order (deterministic)
+  constexpr int U = 8;
+  double acc[U] = {};
+  for (int s0 = threadIdx.x; s0 < p.slots; s0 += 256 * U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + 256 * u;
+      x[u] = s < p.slots ? p.part[(size_t)s * half + m] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] += (double)x[u];
+  }
+  double a = 0.0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) a += acc[u];
+  red[threadIdx.x] = a;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];

@@ -422,8 +422,10 @@ __device__ __forceinline__ void store_dalpha(float* w, float* red, float* slot, 
 }
 
 // Un-rotate one lane's gradient registers (row `row`, columns
-// 32cb + 8rq + 4g + 0..3), add the wedge partials and store float4s.
-template <int D>
+// 32cb + 8rq + 4g + 0..3), add the wedge partials and store float4s (ADD:
+// add them to what `out` holds, a gradient another pass already wrote; the
+// wedge partials are those of this contribution alone).
+template <int D, bool ADD = false>
 __device__ __forceinline__ void finish_rows(f32x16* acc, float scale, const float* part_row,
                                             const float2* cs_row, const void* x_in, size_t x_off,
                                             int bf16, float* out, float pos, float* w, int g) {
@@ -446,6 +448,10 @@ __device__ __forceinline__ void finish_rows(f32x16* acc, float scale, const floa
       load4(x_in, x_off + c, bf16, x);
       w[cb * 8 + rq * 2 + 0] = pos * (x[0] * v[1] - x[1] * v[0]);
       w[cb * 8 + rq * 2 + 1] = pos * (x[2] * v[3] - x[3] * v[2]);
+      if constexpr (ADD) {
+        const float4 o = *reinterpret_cast<const float4*>(out + c);
+        v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+      }
       *reinterpret_cast<float4*>(out + c) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }

@@ -144,13 +144,16 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
  * ROPE_ATTN_STAGE_ALL).  A stage reads what the earlier stages left in the
  * workspace, so the workspace must not be modified in between.
  *   PREP    frequency table; fp16 operand planes (bf16 inputs); D_i (bwd)
- *   EXACT   the float32 path: whole problem (fp32 inputs) or the leading
- *           causal corner, query rows < 128 (bf16 inputs)
+ *   EXACT   the float32 path: whole problem (fp32 inputs); with bf16
+ *           inputs, the forward's leading causal corner (its split-operand
+ *           rows; the backward's corner runs in DQ)
  *   MAIN    forward matrix-core pass (bf16 inputs)
  *   DKDV    dK, dV matrix-core pass (bf16 inputs); with the dS panels it
  *           also writes dS into the workspace
- *   DQ      dQ matrix-core pass (bf16 inputs); with the dS panels it reads
- *           the dS that DKDV left, so DKDV must have run first
+ *   DQ      dQ matrix-core pass (bf16 inputs), and the leading causal
+ *           corner's dQ rows and its shares of dK and dV, which it adds to
+ *           what DKDV wrote; with the dS panels it also reads the dS that
+ *           DKDV left.  DKDV must have run first
  *   DALPHA  fixed-order reduction of the d alpha partials
  *   PREP_GRAD  (backward only, in place of PREP) the dO plane and D_i only:
  *           the frequency table and the Q~, K~, V planes are taken from the
