@@ -282,9 +282,8 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       sp.rows = N;
       sp.bmask = mp.bmask; sp.nb = mp.nb; sp.W = mp.W;
       launch_simt_fwd(sp, hs);
-    } else if (s.corner()) {
-      launch_corner_fwd(mp, hs);
     }
+    // bf16: the corner's split-operand rows run in the MAIN launch
   }
   if ((stages & ROPE_ATTN_STAGE_MAIN) && s.bf16()) launch_fwd_mfma(mp, hs);
   return finish();

@@ -205,7 +205,6 @@ void launch_dq_mfma(const MfmaParams& p, hipStream_t s);
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);
 int dq_mfma_slots(const MfmaParams& p);   // either dQ kernel (p.dsp selects)
 int dkdv_mfma_slots(const MfmaParams& p);
-void launch_corner_fwd(const MfmaParams& p, hipStream_t s);
 void launch_dalpha_reduce(const DalphaParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ device helpers

@@ -59,6 +59,108 @@ __host__ __device__ inline int corner_blocks(const MfmaParams& p) {
   return p.B * p.H * ((p.corner + BM - 1) / BM);
 }
 
+// ------------------------------------------------------------------ forward
+// LDS bytes of the forward's corner body: three 32-row tiles.
+__host__ __device__ constexpr size_t corner_fwd_smem(int D) {
+  return 3 * (size_t)corner_tile_halfs(D, CBN) * 2;
+}
+
+// O and LSE of query rows [128 t, 128 t + 128) below the corner (corner
+// workgroup `bid`), run as the last workgroups of the forward launch.  O is
+// built 32 columns at a time, each pass streaming the keys again (the
+// scores and the softmax statistics come out bit-identical in every pass),
+// so that the body fits the forward's register budget.
+template <int D>
+__device__ __forceinline__ void corner_fwd(const MfmaParams& p, int bid, char* smem) {
+  constexpr int DT = D / 16, CB = D / 32, TILE = corner_tile_halfs(D, CBN);
+  constexpr int CBP = 1;   // column blocks (32 columns) per pass
+  half_t* Kh = reinterpret_cast<half_t*>(smem);
+  half_t* Kl = Kh + TILE;
+  half_t* Vs = Kl + TILE;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int BH = p.B * p.H;
+  const int bh = bid % BH, t = bid / BH;
+  const int q0 = t * BM, wrow0 = q0 + 32 * w, qrow = wrow0 + l32;
+  if (q0 >= p.N) return;  // whole workgroup
+  const int nlo = min(p.N, p.corner);
+  const size_t head = (size_t)bh * p.N * D, lhead = (size_t)bh * p.corner * D;
+
+  half8 qf[DT], ql[DT];
+  load_frag_rows<D>(qf, p.qh + head, qrow, p.N, g);
+  load_frag_rows<D>(ql, p.qlo + lhead, qrow, nlo, g);
+  const int klim = min(qrow, p.N - 1);
+  const int n_kt = min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN);
+  const bool row_ok = qrow < p.N && qrow < p.corner;
+  float* orow = p.o + head + (size_t)qrow * D;
+#pragma unroll 1
+  for (int cb0 = 0; cb0 < CB; cb0 += CBP) {
+    f32x16 o[CBP];
+#pragma unroll
+    for (int c = 0; c < CBP; ++c) o[c] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int k0 = kt * CBN;
+      __syncthreads();
+      stage3<D, CBN>(Kh, p.kh + head, Kl, p.klo + lhead, Vs, p.vh + head, k0, p.N, nlo);
+      __syncthreads();
+      if (k0 > wrow0 + 31) continue;
+      f32x16 s[1];
+      scores<D, 1>(s, Kh, qf, l32, g);
+      scores_add<D, 1>(s, Kl, qf, l32, g);
+      scores_add<D, 1>(s, Kh, ql, l32, g);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 16 * (r >> 3) + 8 * g + (r & 7);
+        const float x = key > klim ? -INFINITY : s[0][r];   // log2 units
+        s[0][r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2_fast(m - ms);
+      float ls = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2_fast(s[0][r] - ms);
+        s[0][r] = pr;
+        ls += pr;
+      }
+      l = l * alpha + ls;
+      m = mn;
+#pragma unroll
+      for (int c = 0; c < CBP; ++c) o[c] *= alpha;
+      half8 ph[2], pl[2];
+      to_frags_split<1>(s, ph, pl);
+#pragma unroll
+      for (int c = 0; c < CBP; ++c) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const half8 a = tr_frag<D>(Vs, tt, cb0 + c, lane);
+          o[c] = mfma(a, ph[tt], o[c]);
+          o[c] = mfma(a, pl[tt], o[c]);
+        }
+      }
+    }
+    const float lt = l + __shfl_xor(l, 32, 64);
+    if (row_ok) {
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int c = 0; c < CBP; ++c) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int col = 32 * (cb0 + c) + 8 * rq + 4 * g;
+          *reinterpret_cast<float4*>(orow + col) =
+              make_float4(o[c][4 * rq] * inv, o[c][4 * rq + 1] * inv, o[c][4 * rq + 2] * inv,
+                          o[c][4 * rq + 3] * inv);
+        }
+      }
+      if (cb0 == 0 && g == 0) p.out_lse[(size_t)bh * p.N + qrow] = (m + __log2f(lt)) * LN2;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dQ
 // dQ of query rows [128 t, 128 t + 128) below the corner (d alpha slot `slot`).
 template <int D>

@@ -310,15 +310,22 @@ constexpr int FBN = 32 * FWD_MB;   // keys per forward step
 template <int D, bool CAUSAL, bool BL>
 __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, FBN>::ALLOC, NB = FWD_NB;
-  __shared__ __attribute__((aligned(16))) half_t Ks[2 * TILE];
-  __shared__ __attribute__((aligned(16))) half_t Vs[2 * TILE];
+  constexpr size_t MAIN = 4 * (size_t)TILE * sizeof(half_t);
+  // the main tiles, or a corner workgroup's tiles (the launch's last ones)
+  __shared__ __attribute__((aligned(16))) char pool[MAIN > corner_fwd_smem(D) ? MAIN : corner_fwd_smem(D)];
   __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the key blocks, ascending
   __shared__ int bcount;
+  const int BH = p.B * p.H;
+  const int ntiles = (p.N + FWD_BM - 1) / FWD_BM, t0 = p.corner / FWD_BM;
+  if ((int)blockIdx.x >= BH * (ntiles - t0)) {   // the corner's split-operand rows
+    if (p.corner > 0) corner_fwd<D>(p, (int)blockIdx.x - BH * (ntiles - t0), pool);
+    return;
+  }
+  half_t* Ks = reinterpret_cast<half_t*>(pool);
+  half_t* Vs = Ks + 2 * TILE;
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int BH = p.B * p.H;
-  const int ntiles = (p.N + FWD_BM - 1) / FWD_BM, t0 = p.corner / FWD_BM;
   int bh, t;
   map_block(blockIdx.x, BH, ntiles - t0, true, bh, t);
   t += t0;
@@ -893,8 +900,11 @@ int dkdv_mfma_slots(const MfmaParams& p) { return dkdv_blocks(p); }
     else RA_LAUNCH1(KERNEL, false);                                                            \
   } while (0)
 
+// The forward launch: the row tiles past the corner, heaviest first, then
+// the corner's split-operand workgroups (beside the lightest tiles).
 void launch_fwd_mfma(const MfmaParams& p, hipStream_t s) {
-  const int nb = p.B * p.H * max(0, (p.N + FWD_BM - 1) / FWD_BM - p.corner / FWD_BM);
+  const int nb = p.B * p.H * max(0, (p.N + FWD_BM - 1) / FWD_BM - p.corner / FWD_BM) +
+                 (p.corner ? corner_blocks(p) : 0);
   if (nb > 0) RA_LAUNCH(fwd_kernel, nb);
 }
 // The corner workgroups (latency-bound chains of a few to a few tens of

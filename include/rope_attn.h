@@ -144,10 +144,11 @@ int rope_attn_bwd(const void* q, const void* k, const void* v, const float* o, c
  * ROPE_ATTN_STAGE_ALL).  A stage reads what the earlier stages left in the
  * workspace, so the workspace must not be modified in between.
  *   PREP    frequency table; fp16 operand planes (bf16 inputs); D_i (bwd)
- *   EXACT   the float32 path: whole problem (fp32 inputs); with bf16
- *           inputs, the forward's leading causal corner (its split-operand
- *           rows; the backward's corner runs in DQ)
- *   MAIN    forward matrix-core pass (bf16 inputs)
+ *   EXACT   the float32 path: the whole problem (fp32 inputs); nothing
+ *           with bf16 inputs (their leading causal corner runs in MAIN and
+ *           in DQ)
+ *   MAIN    forward matrix-core pass (bf16 inputs), the leading causal
+ *           corner's split-operand rows included
  *   DKDV    dK, dV matrix-core pass (bf16 inputs); with the dS panels it
  *           also writes dS into the workspace
  *   DQ      dQ matrix-core pass (bf16 inputs), and the leading causal
