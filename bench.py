@@ -43,17 +43,28 @@ METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
 # Stage bits of the C ABI (rope_attn_stage)
 PREP, EXACT, MAIN, DKDV, DQ, DALPHA, PREP_GRAD = 1, 2, 4, 8, 16, 32, 64
 # The timed step: the whole forward in one call, the backward in four calls,
-# split where a kernel is timed on its own: prep (PREP_GRAD: only dO and D,
-# reusing the forward's table and operand planes from the shared workspace)
-# and the exact corner; dK/dV (which also writes the dS panels); dQ (from
-# the panels); the d alpha reduction.
+# split where a kernel is timed on its own: prep (PREP_GRAD: only the dO maxima,
+# the scaled dO plane and D, reusing the forward's table and operand planes
+# from the shared workspace); dK/dV (which also writes the dS panels); dQ (from
+# the panels, with the split-operand corner's backward as its last
+# workgroups); the d alpha reduction.  EXACT is the float32 path: with bf16
+# inputs it does nothing, with fp32 inputs it is the whole pass.
 FWD_CALLS = [("fwd", PREP | EXACT | MAIN)]
-BWD_CALLS = [("bwd_prep_exact", PREP_GRAD | EXACT), ("bwd_dkdv", DKDV), ("bwd_dq", DQ),
+BWD_CALLS = [("bwd_prep", PREP_GRAD | EXACT), ("bwd_dkdv", DKDV), ("bwd_dq", DQ),
              ("bwd_dalpha", DALPHA)]
-# every kernel in its own call (serial), timed after the timed step for the breakdown
-FWD_STAGES = [("fwd_prep", PREP), ("fwd_exact", EXACT), ("fwd_main", MAIN)]
-BWD_STAGES = [("bwd_prep", PREP_GRAD), ("bwd_exact", EXACT), ("bwd_dkdv", DKDV), ("bwd_dq", DQ),
-              ("bwd_dalpha", DALPHA)]
+
+
+def stage_lists(dtype):
+    """Every kernel in its own call (serial), timed after the timed step for
+    the breakdown; the EXACT stage only where it runs (fp32 inputs)."""
+    if dtype == "bf16":
+        return ([("fwd_prep", PREP), ("fwd_main", MAIN)],
+                [("bwd_prep", PREP_GRAD), ("bwd_dkdv", DKDV), ("bwd_dq", DQ),
+                 ("bwd_dalpha", DALPHA)])
+    return ([("fwd_prep", PREP), ("fwd_exact", EXACT)],
+            [("bwd_prep", PREP_GRAD), ("bwd_exact", EXACT), ("bwd_dalpha", DALPHA)])
+
+
 # algorithmic products of the dominant matrix-core kernel (units of B H N^2 D
 # flops, causal): dV, dP and dK
 DOMINANT = ("bwd_dkdv", "dkdv_kernel", 3.0)
@@ -90,7 +101,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("mfma.hip", "tile.h", "common.h")
+KERNEL_SOURCES = ("mfma.hip", "tile.h", "corner.h", "common.h")
 
 
 def kernel_source_hash() -> str:
@@ -360,7 +371,8 @@ def main():
                        device=dev)
     ws_f = ws_b
 
-    names = [n for n, _ in FWD_STAGES] + [n for n, _ in BWD_STAGES]
+    fwd_stages, bwd_stages = stage_lists(wl.dtype)
+    names = [n for n, _ in fwd_stages] + [n for n, _ in bwd_stages]
     opts = None
     if args.unrotated_pairs or args.scale or args.pos_offset:
         opts = dict(unrotated_pairs=args.unrotated_pairs, scale=args.scale,
@@ -429,7 +441,7 @@ def main():
     nd = min(args.steps, 5)
     evd = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nd)]
     for s in range(nd):
-        step(FWD_STAGES, BWD_STAGES, evd[s])
+        step(fwd_stages, bwd_stages, evd[s])
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([evd[s][i].elapsed_time(evd[s][i + 1]) for s in range(nd)]))
                 for i, n in enumerate(names)}
