@@ -3,6 +3,7 @@
 // file-scope device array, one copy per GPU, instead of a caller buffer.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 
 #include <mutex>
@@ -43,7 +44,8 @@ extern "C" int rope_attn_fwd_noalloc(const void* q, const void* k, const void* v
   const size_t need = rope_attn_fwd_workspace_bytes(B, H, N, D, dtype, causal);
   const auto bad_ptr = [](const void* p) { return !p || ((uintptr_t)p & 15u) != 0; };
   if (need == 0 || bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o) || bad_ptr(lse) ||
-      ((uintptr_t)alpha & 15u) != 0)
+      ((uintptr_t)alpha & 15u) != 0 || !(base > 0.0) || !isfinite(base) ||
+      (causal != 0 && causal != 1))
     // invalid arguments: the forward's own validation names them (before any HIP call)
     return rope_attn_fwd_ex(ROPE_ATTN_STAGE_ALL, nullptr, q, k, v, o, lse, B, H, N, D, dtype, base,
                             alpha, causal, nullptr, 0, stream);

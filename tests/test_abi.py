@@ -266,3 +266,7 @@ def test_noalloc_validation(lib):
     assert lib.rope_attn_fwd_noalloc(None, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 1, None) == -1
     # 1 x 64 x 8192 x 128 bf16 needs ~390 MiB of workspace, past the 64 MiB array
     assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 64, 8192, 128, 1, 1e4, None, 1, None) == -5
+    # base and causal are checked before the device's array is looked up
+    assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 1, 16, 64, 1, 0.0, None, 1, None) == -7
+    assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 1, 16, 64, 1, float("nan"), None, 1, None) == -7
+    assert lib.rope_attn_fwd_noalloc(A, A, A, A, A, 1, 1, 16, 64, 1, 1e4, None, 2, None) == -7
