@@ -37,7 +37,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_TFLOPS = 2516.6   # fp16 / bf16 dense matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
 HBM_GBS = 8000.0
-FP32_VECTOR_TFLOPS = 157.3   # vector fp32: 256 CU x 128 FMA lanes x 2 flops x 2.4 GHz
+FP32_MFMA_TFLOPS = 157.3     # fp32 matrix cores: 256 CU x 256 flop/clk x 2.4 GHz (the vector rate too)
 METRIC = "causal RoPE-attn fwd+bwd TFLOP/s and % bf16 MFMA peak, n=8192 d_h=128"
 
 # Stage bits of the C ABI (rope_attn_stage)
@@ -478,10 +478,10 @@ def main():
                    or _lib.workspace_bytes("bwd", B, H, N, D, dt_code, wl.causal)
                    == _lib.workspace_bytes("bwd_min", B, H, N, D, dt_code, wl.causal) else "ds_panels")
     else:
-        # fp32 inputs: the exact float32 path runs the whole step on the vector ALUs
-        roofline = {"bound": "alu", "kernel": "simt (whole step, fp32 FMA)", "achieved": round(value, 4),
-                    "peak": FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(value / FP32_VECTOR_TFLOPS, 5), "traffic": None,
+        # fp32 inputs: the float32 path runs the whole step on the fp32 matrix cores
+        roofline = {"bound": "mfma", "kernel": "f32 path (whole step, v_mfma_f32_32x32x2f32)",
+                    "achieved": round(value, 4), "peak": FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(value / FP32_MFMA_TFLOPS, 5), "traffic": None,
                     "avg_ms": round(ms_step, 4)}
         dq_pass = "fp32_exact"
     line = {

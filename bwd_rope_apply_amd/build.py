@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librope_attn.so")
 EXAMPLE = os.path.join(HERE, "rope_attn_example")
 CLOCK_LIB = os.path.join(HERE, "libra_clock.so")
-SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "gram.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "prep.hip", "simt.hip", "f32mfma.hip", "mfma.hip", "gram.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -281,7 +281,8 @@ int rope_attn_fwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       sp.scale = op.scale;
       sp.rows = N;
       sp.bmask = mp.bmask; sp.nb = mp.nb; sp.W = mp.W;
-      launch_simt_fwd(sp, hs);
+      if (sp.bmask) launch_simt_fwd(sp, hs);   // block lists: the vector path
+      else launch_f32_fwd(sp, hs);
     }
     // bf16: the corner's split-operand rows run in the MAIN launch
   }
@@ -395,9 +396,11 @@ int rope_attn_bwd_ex(unsigned stages, const rope_attn_options* opts, const void*
       sp.rows = N; sp.qend = N; sp.final_ = 1;
       sp.bmask = mp.bmask; sp.nb = mp.nb; sp.W = mp.W;
       sp.slot0 = 0;
-      launch_simt_dq(sp, hs);
+      if (sp.bmask) launch_simt_dq(sp, hs);   // block lists: the vector path
+      else launch_f32_dq(sp, hs);
       sp.slot0 = n_exact_dq;
-      launch_simt_dkdv(sp, hs);
+      if (sp.bmask) launch_simt_dkdv(sp, hs);
+      else launch_f32_dkdv(sp, hs);
     }
     // bf16: the corner runs in the dQ launch (DQ stage)
   }

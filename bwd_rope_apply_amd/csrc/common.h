@@ -200,6 +200,10 @@ void launch_simt_fwd(const SimtParams& p, hipStream_t s);
 void launch_simt_dq(const SimtParams& p, hipStream_t s);
 void launch_simt_dkdv(const SimtParams& p, hipStream_t s);
 int simt_slots(int BH, int rows);       // dalpha slots used by one simt dq/dkdv launch
+// the fp32 path on the matrix cores (dense attention; the same slots as simt)
+void launch_f32_fwd(const SimtParams& p, hipStream_t s);
+void launch_f32_dq(const SimtParams& p, hipStream_t s);
+void launch_f32_dkdv(const SimtParams& p, hipStream_t s);
 void launch_fwd_mfma(const MfmaParams& p, hipStream_t s);
 void launch_dq_mfma(const MfmaParams& p, hipStream_t s);
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s);

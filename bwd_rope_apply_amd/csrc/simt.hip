@@ -1,6 +1,7 @@
-// Exact fp32 path: plain fused multiply-adds, one row per group of four
-// lanes (each lane owns D/4 consecutive columns, so every rotation pair stays
-// inside one lane).  It serves every call with fp32 inputs.
+// Exact fp32 path on the vector ALUs: plain fused multiply-adds, one row per
+// group of four lanes (each lane owns D/4 consecutive columns, so every
+// rotation pair stays inside one lane).  It serves fp32 calls with block
+// lists; dense fp32 calls take the matrix-core path (f32mfma.hip).
 //
 // Forward: S = Q~ K~^T / sqrt(D) with the causal mask j <= i, the
 // normalised softmax s(x), O = P V and the row log-sum-exp ("RoPE attention

@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bwd_rope_apply_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "prep.hip", "simt.hip", "mfma.hip", "gram.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "prep.hip", "simt.hip", "f32mfma.hip", "mfma.hip", "gram.hip", "noalloc.hip"]
 # every -fsanitize applies to the host pass alone
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
