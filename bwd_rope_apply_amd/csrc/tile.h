@@ -45,22 +45,22 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Block index -> (head, tile).  Workgroups are dispatched round-robin over
 // the 8 XCDs; when the head count allows, each XCD gets a fixed set of heads
 // so that their K/V (or Q/dO) tiles stay in that XCD's L2.  Tiles are issued
-// heaviest first (most causal work).  An XCD with more than HGROUP heads
-// works through them HGROUP at a time (heaviest first within each group), so
-// that fewer heads' streamed tiles compete for its L2 at once (measured at
-// 4 x 32 x 4096: dK/dV -2.5%, dQ from panels -5.6% against all 16 heads
-// interleaved).
-constexpr int HGROUP = 4;
+// heaviest first (most causal work).  An XCD with more than `group` heads
+// works through them `group` at a time (heaviest first within each group),
+// so that fewer heads' streamed tiles compete for its L2 at once (measured
+// at 4 x 32 x 4096 with groups of 4: dK/dV -2.5%, dQ from panels -5.6%
+// against all 16 heads interleaved; groups of 2 made the forward and the
+// dQ product slower at 1 x 32 x 8192 and left dK/dV unchanged).
 __device__ __forceinline__ void map_block(int idx, int BH, int ntiles, bool heavy_high, int& bh,
-                                          int& t) {
+                                          int& t, int group = 4) {
   int k;
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;
     const int x = idx & 7, s = idx >> 3;
-    if (hpx > HGROUP && hpx % HGROUP == 0) {
-      const int per = HGROUP * ntiles, grp = s / per, within = s % per;
-      bh = x * hpx + grp * HGROUP + within % HGROUP;
-      k = within / HGROUP;
+    if (hpx > group && hpx % group == 0) {
+      const int per = group * ntiles, grp = s / per, within = s % per;
+      bh = x * hpx + grp * group + within % group;
+      k = within / group;
     } else {
       bh = x * hpx + s % hpx;
       k = s / hpx;
