@@ -1,7 +1,7 @@
 """The C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer
 (no GPU): the library's sources are compiled with both sanitizers on their
 host pass (the device code as usual), linked with tests/abi_host_check.cpp,
-and run.  The driver makes only calls
+and run.  The check program makes only calls
 that validation rejects, or pure workspace-size queries, so no kernel is
 launched; any sanitizer report aborts it."""
 import os
