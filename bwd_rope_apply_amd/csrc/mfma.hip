@@ -737,11 +737,13 @@ constexpr int DQP_TS = DQP_KB * PANEL;   // halfs per panel tile (16 KiB)
 #endif
 constexpr int DQP_STAGES = RA_DQP_STAGES;
 
-template <int D, bool CAUSAL>
+// NJ: 32-row query blocks per wave, 2 (a whole panel per workgroup) or 1 (half
+// a panel, for launches too small to fill the GPU otherwise).
+template <int D, bool CAUSAL, int NJ>
 __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) {
-  constexpr int CB = D / 32, TK = TileDMA<D, DQP_KB>::ALLOC, TS = DQP_TS;
+  constexpr int CB = D / 32, TK = TileDMA<D, DQP_KB>::ALLOC, TS = DQP_TS * NJ / 2;
   constexpr int NS = DQP_STAGES;
-  static_assert(TS * 2 == 16 * 1024, "four 1 KiB copies per wave per panel tile");
+  static_assert(TS * 2 == NJ * 8 * 1024, "2 NJ 1 KiB copies per wave per panel tile");
   constexpr size_t MAIN = (size_t)NS * (TK + TS) * sizeof(half_t);
   // the ring, or a corner workgroup's tiles (the launch's first ones)
   __shared__ __attribute__((aligned(16))) char pool[MAIN > corner_bwd_smem(D) ? MAIN : corner_bwd_smem(D)];
@@ -752,7 +754,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
     corner_bwd<D>(p, bx - p.corner_at, pool);
     return;
   }
-  const int mb = bx < p.corner_at ? bx : bx - ncorner;   // this workgroup's panel
+  const int mb = bx < p.corner_at ? bx : bx - ncorner;   // this workgroup's panel (half)
   half_t* Ks = reinterpret_cast<half_t*>(pool);
   half_t* Ss = Ks + NS * TK;
 
@@ -760,51 +762,53 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
   const int l32 = lane & 31, g = lane >> 5;
   const int BH = p.B * p.H;
   const int np = n_panels(p.N), t0 = p.corner / PANEL;
-  int bh, t;
-  map_block(mb, BH, np - t0, true, bh, t);
+  int bh, u;
+  map_block(mb, BH, (np - t0) * (2 / NJ), true, bh, u);
   const int slot = p.slot0 + ncorner + mb;
-  t += t0;
-  const int q0 = t * PANEL, wrow0 = q0 + 64 * w;
+  const int t = u / (2 / NJ) + t0, hb = NJ == 1 ? (u & 1) : 0;   // panel, half
+  const int q0 = t * PANEL + 128 * hb, wrow0 = q0 + 32 * NJ * w;
   const size_t head = (size_t)bh * p.N * D;
   const half_t* kh = p.kh + head;
   const half_t* panel = p.dsp + (size_t)bh * panel_head(p.N, CAUSAL) + panel_off(t, p.N, CAUSAL);
-  const bool active = wrow0 + 64 > p.corner && wrow0 < p.N;
+  const bool active = wrow0 + 32 * NJ > p.corner && wrow0 < p.N;
   // keys of this panel below N, in whole tiles (the panel rows are a
   // multiple of the tile; a ragged last tile holds zeros past N)
   const int nkeys = min(panel_rows(t, p.N, CAUSAL), (p.N + DQP_KB - 1) / DQP_KB * DQP_KB);
   const int n_kt = nkeys / DQP_KB;
 
-  f32x16 acc[2][CB];
+  f32x16 acc[NJ][CB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[j][cb] = f32x16{};
   }
   TileDMA<D, DQP_KB> dmk;
   dmk.init(lane, w);
   const int wave = w;
-  // this lane's fragment offsets in a ring slot (its wave's query blocks 2w, 2w + 1)
-  const int pf_lane = 2048 * w + panel_lane_offset(lane), tr_lane = tr_lane_offset<D>(lane);
-  // Copies this wave issues per tile: KLO or KLO + 1 for K~, 4 for the panel.
+  // this lane's fragment offsets in a ring slot (its wave's NJ query blocks)
+  const int pf_lane = 1024 * NJ * w + panel_lane_offset(lane), tr_lane = tr_lane_offset<D>(lane);
+  // Copies this wave issues per tile: KLO or KLO + 1 for K~, 2 NJ for the panel.
   // Every outstanding vector memory operation of the loop is such a copy, so
   // "tile i landed" is "at most (copies per tile) x (tiles issued after i)
   // outstanding".  In the steady state NS - 2 tiles stay in flight; the last
   // steps wait for everything.
   constexpr int KLO = TileDMA<D, DQP_KB>::NBLK / 4;
-  static_assert((KLO + 5) * (NS - 2) < 64, "vmcnt range");
+  constexpr int PC = 2 * NJ;   // panel copies per wave per tile
+  static_assert((KLO + 1 + PC) * (NS - 2) < 64, "vmcnt range");
   const bool khi = dmk.count() > KLO;
   auto wait_landed = [&](bool steady) {
     if (!steady) wait_vm_const<0>();
-    else if (khi) wait_vm_const<(KLO + 5) * (NS - 2)>();
-    else wait_vm_const<(KLO + 4) * (NS - 2)>();
+    else if (khi) wait_vm_const<(KLO + 1 + PC) * (NS - 2)>();
+    else wait_vm_const<(KLO + PC) * (NS - 2)>();
   };
   auto load = [&](int kt) {
     const int b = kt % NS;
     dmk.load(Ks + b * TK, kh, kt * DQP_KB);
-    // the panel tile: 1 KiB blocks wave + 4 i, lane l at byte 16 l
-    const uint32_t tb = (uint32_t)kt * (uint32_t)(2 * DQP_TS);
+    // the panel tile (this half's query blocks): 1 KiB blocks wave + 4 i,
+    // lane l at byte 16 l
+    const uint32_t tb = (uint32_t)kt * (uint32_t)(2 * DQP_TS) + 8192u * (uint32_t)hb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < PC; ++i)
       lds_copy16_nt(panel, tb + 1024u * (wave + 4 * i) + 16u * lane, Ss + b * TS + (wave + 4 * i) * 512);
   };
 #pragma unroll
@@ -822,16 +826,16 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
     // into the buffer every wave finished reading before the last barrier
     if (kt + NS - 1 < n_kt) load(kt + NS - 1);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tiles' copies ahead of the compute
-    if (active && !(CAUSAL && k0 > wrow0 + 63)) {
+    if (active && !(CAUSAL && k0 > wrow0 + 32 * NJ - 1)) {
       // every fragment of the step first (one address add per operand, the
       // rest in the reads' offsets), then the products
       const half_t* pb = Ss + cs + pf_lane;
       const half_t* kb = Ks + ck + tr_lane;
-      half8 bf[DQP_KB / 16][2], af[DQP_KB / 16][CB];
+      half8 bf[DQP_KB / 16][NJ], af[DQP_KB / 16][CB];
 #pragma unroll
       for (int ts = 0; ts < DQP_KB / 16; ++ts) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bf[ts][j] = tr_pair<64>(pb + 1024 * j + 256 * ts);
+        for (int j = 0; j < NJ; ++j) bf[ts][j] = tr_pair<64>(pb + 1024 * j + 256 * ts);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) af[ts][cb] = tr_pair<8 * (D + 8)>(kb + 16 * ts * (D + 8) + 32 * cb);
       }
@@ -839,8 +843,8 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
       for (int ts = 0; ts < DQP_KB / 16; ++ts) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          acc[0][cb] = mfma(af[ts][cb], bf[ts][0], acc[0][cb]);
-          acc[1][cb] = mfma(af[ts][cb], bf[ts][1], acc[1][cb]);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[j][cb] = mfma(af[ts][cb], bf[ts][j], acc[j][cb]);
         }
       }
     }
@@ -852,7 +856,7 @@ __global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) 
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int qrow = wrow0 + 32 * j + l32;
     if (active && qrow >= p.corner && qrow < p.N) {
       finish_rows<D>(acc[j], p.scale * dscale_inv(p.dsc, bh), nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
@@ -870,9 +874,16 @@ int fwd_blocks(const MfmaParams& p) {  // dQ workgroups: 128-row tiles past the 
   return tiles > 0 ? p.B * p.H * tiles : 0;
 }
 int dkdv_blocks(const MfmaParams& p) { return p.B * p.H * ((p.N + BM - 1) / BM); }
-int dq_panel_blocks(const MfmaParams& p) {  // panels past the corner
+// The dQ product takes half a panel per workgroup when whole panels would
+// leave the GPU short of workgroups (fewer than two per CU of a 256-CU part).
+constexpr int DQP_HALF_BELOW = 512;
+bool dq_panel_half(const MfmaParams& p) {
   const int np = n_panels(p.N) - p.corner / PANEL;
-  return np > 0 ? p.B * p.H * np : 0;
+  return (long)p.B * p.H * np < DQP_HALF_BELOW;
+}
+int dq_panel_blocks(const MfmaParams& p) {  // panels (halves) past the corner
+  const int np = n_panels(p.N) - p.corner / PANEL;
+  return np > 0 ? p.B * p.H * np * (dq_panel_half(p) ? 2 : 1) : 0;
 }
 
 }  // namespace
@@ -922,8 +933,13 @@ void launch_dq_mfma(const MfmaParams& p_in, hipStream_t s) {
     const int nb = dq_corner_blocks(p) + dq_panel_blocks(p);
     const dim3 grid((unsigned)nb), block(256);
     if (nb <= 0) return;
-    if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dq_panel_kernel<128, false>), grid, block, 0, s, p);
+    if (dq_panel_half(p)) {
+      if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true, 1>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((dq_panel_kernel<128, false, 1>), grid, block, 0, s, p);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((dq_panel_kernel<128, false, 2>), grid, block, 0, s, p);
+    }
     return;
   }
   p.corner_at = fwd_blocks(p);

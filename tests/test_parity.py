@@ -263,6 +263,13 @@ def test_bf16_panels_batches(B, H, N, causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
+def test_bf16_panels_whole_panel_mode_ragged(causal):
+    """Enough heads that the dQ product takes whole panels per workgroup
+    (launches of fewer panels take half panels), at a ragged length."""
+    _check(W.make_inputs(W.get("layer_2k", B=4, H=128, N=300, seed=4300)), causal=causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
 def test_panels_and_recomputation_agree(causal):
     """The two dQ passes on the same inputs: dK and dV come from the same
     dK/dV kernel arithmetic (bit-identical); dQ and dalpha sum the same dS
