@@ -18,39 +18,24 @@ namespace ra {
 
 namespace {
 
-// Tiling (compile-time; the defaults are the measured best on MI355X):
+// Tiling (the measured best on MI355X):
 //   *_WPS   waves per SIMD the register budget is sized for (more waves
 //           let one wave's softmax VALU work overlap another's MFMAs; the
 //           512 VGPRs of a SIMD lane are shared among them)
-//   *_BN    rows of the streamed operand per loop step (multiple of 32)
+//   *_BN    rows of the streamed operand per product (multiple of 32)
 //   FWD_NB  32-row query blocks per forward wave
 //   FWD_MB  32-key blocks per forward step (1: 32-key tiles, whose smaller
 //           registers and LDS allow 3 waves per SIMD)
-#ifndef RA_FWD_NB
-#define RA_FWD_NB 1
-#endif
-#ifndef RA_FWD_WPS
-#define RA_FWD_WPS 3
-#endif
-#ifndef RA_FWD_MB
-#define RA_FWD_MB 1        // 32-key blocks per forward step
-#endif
-#ifndef RA_DQ_BN
-#define RA_DQ_BN 32
-#endif
-#ifndef RA_DQ_SUB
-#define RA_DQ_SUB 2        // RA_DQ_BN-key products per copied tile (one barrier per tile)
-#endif
-#ifndef RA_DQ_WPS
-#define RA_DQ_WPS 2
-#endif
-#ifndef RA_DKDV_BN
-#define RA_DKDV_BN 32
-#endif
-#ifndef RA_DKDV_WPS
-#define RA_DKDV_WPS 2
-#endif
-
+//   DQ_SUB  DQ_BN-key products per copied tile in the recomputing dQ
+//           (one barrier per tile)
+constexpr int FWD_NB = 1;
+constexpr int FWD_WPS = 3;
+constexpr int FWD_MB = 1;
+constexpr int DQ_BN = 32;
+constexpr int DQ_SUB = 2;
+constexpr int DQ_WPS = 2;
+constexpr int DKDV_BN = 32;
+constexpr int DKDV_WPS = 2;
 
 // One step of the forward (MB blocks of 32 keys) for one wave owning NB
 // blocks of 32 query rows: scores, online softmax, O += P V.  Every K~ and
@@ -302,13 +287,11 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
 // the loop streams FBN-key tiles of K~ and V through double-buffered LDS,
 // the next tile's copies in flight while the current tile is computed.
 // Rows below the exact corner are skipped.
-constexpr int FWD_NB = RA_FWD_NB;
 constexpr int FWD_BM = 4 * 32 * FWD_NB;
-constexpr int FWD_MB = RA_FWD_MB;
 constexpr int FBN = 32 * FWD_MB;   // keys per forward step
 
 template <int D, bool CAUSAL, bool BL>
-__global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
+__global__ __launch_bounds__(256, FWD_WPS) void fwd_kernel(MfmaParams p) {
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, FBN>::ALLOC, NB = FWD_NB;
   constexpr size_t MAIN = 4 * (size_t)TILE * sizeof(half_t);
   // the main tiles, or a corner workgroup's tiles (the launch's last ones)
@@ -432,8 +415,8 @@ __global__ __launch_bounds__(256, RA_FWD_WPS) void fwd_kernel(MfmaParams p) {
 // At D = 64 the operands and accumulators take half the registers: three
 // waves per SIMD fit (measured at 1 x 8 x 32768 x 64: 1.493 vs 1.557 ms with two).
 template <int D, bool CAUSAL, bool BL>
-__global__ __launch_bounds__(256, (D == 64 ? 3 : RA_DQ_WPS)) void dq_kernel(MfmaParams p) {
-  constexpr int SB = RA_DQ_BN, NMB = SB / 32, KB = SB * RA_DQ_SUB;
+__global__ __launch_bounds__(256, (D == 64 ? 3 : DQ_WPS)) void dq_kernel(MfmaParams p) {
+  constexpr int SB = DQ_BN, NMB = SB / 32, KB = SB * DQ_SUB;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, KB>::ALLOC;
   constexpr size_t MAIN = 4 * (size_t)TILE * sizeof(half_t);
   // the main tiles, or a corner workgroup's tiles (the launch's first ones)
@@ -513,7 +496,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : RA_DQ_WPS)) void dq_kernel(Mfma
     walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
 #pragma unroll
-    for (int sub = 0; sub < RA_DQ_SUB; ++sub) {
+    for (int sub = 0; sub < DQ_SUB; ++sub) {
       // rows SB sub .. of the tile: the row layout keeps each 32-row half whole
       const int ks = k0 + SB * sub;
       if (!(CAUSAL && ks > wrow0 + 31))
@@ -547,8 +530,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : RA_DQ_WPS)) void dq_kernel(Mfma
 // writes dS into the panels for the dQ product (zeros for the pairs of
 // a step that a wave skips as wholly masked, which that product reads).
 template <int D, bool CAUSAL, bool BL, bool DS>
-__global__ __launch_bounds__(256, RA_DKDV_WPS) void dkdv_kernel(MfmaParams p) {
-  constexpr int QB = RA_DKDV_BN, NMB = QB / 32;
+__global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
+  constexpr int QB = DKDV_BN, NMB = QB / 32;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, QB>::ALLOC;
   __shared__ __attribute__((aligned(16))) half_t Qs[2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Ds[2 * TILE];
@@ -732,15 +715,12 @@ __device__ __forceinline__ int panel_lane_offset(int lane) {
 // corner only help load.
 constexpr int DQP_KB = 32;
 constexpr int DQP_TS = DQP_KB * PANEL;   // halfs per panel tile (16 KiB)
-#ifndef RA_DQP_STAGES
-#define RA_DQP_STAGES 3
-#endif
-constexpr int DQP_STAGES = RA_DQP_STAGES;
+constexpr int DQP_STAGES = 3;
 
 // NJ: 32-row query blocks per wave, 2 (a whole panel per workgroup) or 1 (half
 // a panel, for launches too small to fill the GPU otherwise).
 template <int D, bool CAUSAL, int NJ>
-__global__ __launch_bounds__(256, RA_DQ_WPS) void dq_panel_kernel(MfmaParams p) {
+__global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
   constexpr int CB = D / 32, TK = TileDMA<D, DQP_KB>::ALLOC, TS = DQP_TS * NJ / 2;
   constexpr int NS = DQP_STAGES;
   static_assert(TS * 2 == NJ * 8 * 1024, "2 NJ 1 KiB copies per wave per panel tile");
