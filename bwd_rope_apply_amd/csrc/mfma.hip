@@ -529,22 +529,34 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : DQ_WPS)) void dq_kernel(MfmaPar
 // workgroup's V rows stay in LDS (natural layout) and feed dP.  DS also
 // writes dS into the panels for the dQ product (zeros for the pairs of
 // a step that a wave skips as wholly masked, which that product reads).
-template <int D, bool CAUSAL, bool BL, bool DS>
-__global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
+// G: query groups.  G = 2 (launches too small to give every CU two
+// workgroups) splits each workgroup's query range between two groups of 4
+// waves on the same 128 keys, each streaming its own tiles; the second
+// group's dK, dV are added to the first's through LDS at the end (a fixed
+// order), so the per-workgroup chain of steps is half as long.
+template <int D, bool CAUSAL, bool BL, bool DS, int G = 1>
+__global__ __launch_bounds__(256 * G, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
+  static_assert(G == 1 || (G == 2 && !BL), "query groups: dense attention only");
   constexpr int QB = DKDV_BN, NMB = QB / 32;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, QB>::ALLOC;
-  __shared__ __attribute__((aligned(16))) half_t Qs[2 * TILE];
-  __shared__ __attribute__((aligned(16))) half_t Ds[2 * TILE];
+  // each group's double-buffered Q~ and dO tiles; G = 2 also reuses them
+  // for the dK, dV hand-over (4 waves x 64 lanes x 64 floats)
+  static_assert(G == 1 || 2 * G * 2 * TILE * 2 >= 4 * 64 * (D / 2) * 4, "hand-over fits the tiles");
+  __shared__ __attribute__((aligned(16))) half_t tiles[G * 2 * 2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vst[BM * (D + 8)];
-  __shared__ __attribute__((aligned(16))) float rsl[2 * 2 * QB];
-  __shared__ float red[4 * (D / 2)];
+  __shared__ __attribute__((aligned(16))) float rsl[G * 2 * 2 * QB];
+  __shared__ float red[4 * G * (D / 2)];
   __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the query blocks, ascending
   __shared__ uint32_t bcol[BL ? MAX_BLOCKS / 32 : 1];
   __shared__ int bcount;
 
   // the wave index as a scalar: per-wave skips and panel addresses stay uniform
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wg >> 2, w = wg & 3;   // query group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
+  half_t* const Qs = tiles + grp * 4 * TILE;
+  half_t* const Ds = Qs + 2 * TILE;
+  float* const rsg = rsl + grp * 2 * 2 * QB;
   const int BH = p.B * p.H;
   const int ntiles = (p.N + BM - 1) / BM;
   int bh, t;
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   half8 kf[DT];
   load_frag_rows<D>(kf, p.kh + head, key, p.N, g);
   // rows k0 .. k0 + 127 of V, padded rows; lane reads row 32 w + l32
-  for (int ch = threadIdx.x; ch < BM * (D / 8); ch += 256) {
+  for (int ch = threadIdx.x; ch < BM * (D / 8); ch += 256 * G) {
     const int r = ch / (D / 8), c8 = ch % (D / 8);
     const int row = min(k0 + r, p.N - 1);
     *reinterpret_cast<half8*>(Vst + r * (D + 8) + c8 * 8) =
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   int n_it;
   if constexpr (BL) {
     static_assert(BM == BLK && BLK % QB == 0, "one key block per workgroup");
-    const int cnt = column_blocks<256>(p.bmask, p.nb, p.W, bh, t, qs0 / BLK, bcol, blist, &bcount);
+    const int cnt = column_blocks<256 * G>(p.bmask, p.nb, p.W, bh, t, qs0 / BLK, bcol, blist, &bcount);
     n_it = 0;
     if (cnt > 0) {
       const int rows = min(BLK, p.N - blist[cnt - 1] * BLK);
@@ -590,8 +602,11 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   } else {
     n_it = qs0 < p.N ? (p.N - qs0 + QB - 1) / QB : 0;
   }
+  // this group's steps: [0, h) for group 0, [h, n_it) for group 1
+  const int h = G == 1 ? n_it : (n_it + 1) / 2;
+  const int g_first = grp ? h : 0, n_g = grp ? n_it - h : h;
   Walk<QB, BL> walk;
-  walk.init(blist, qs0, n_it);
+  walk.init(blist, qs0 + g_first * QB, n_g);
 
   TileDMA<D, QB> dma;
   dma.init(lane, w);
@@ -601,13 +616,14 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     dma.load(Qs + buf * TILE, qh, r0);
     dma.load(Ds + buf * TILE, doh, r0);
     if (dma.wave < NMB)
-      lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane_here(), rsl + buf * 2 * QB + dma.wave * 64);
+      lds_copy4(rs_h + ((r0 >> 5) + dma.wave) * 64, 4u * lane_here(), rsg + buf * 2 * QB + dma.wave * 64);
   };
-  if (n_it > 0) load_rows(walk.cur, 0);
+  if (n_g > 0) load_rows(walk.cur, 0);
   wait_lds_copies();
   __syncthreads();
   // the first steps cross the workgroup's diagonal (masked), the rest need
-  // no mask: peeled loops, one inlined tile body each
+  // no mask: peeled loops, one inlined tile body each (with G = 2 the second
+  // group runs its first steps through the masked body too, which is exact)
   int n_masked;
   if constexpr (BL)
     n_masked = (CAUSAL && n_it > 0 && blist[0] == t) ? min(n_it, SPB) : 0;
@@ -638,9 +654,13 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
     }
   };
   auto step = [&](int it, auto masked) {
+    if (G > 1 && it >= n_g) {   // this group is done: keep the barriers in step
+      __syncthreads();
+      return;
+    }
     const int r0 = walk.cur;
     const int cur = it & 1;
-    if (it + 1 < n_it) load_rows(walk.next, cur ^ 1);
+    if (it + 1 < n_g) load_rows(walk.next, cur ^ 1);
     walk.prefetch(it);
     flush_ds();
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
@@ -649,7 +669,7 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
                                (size_t)(r0 % PANEL) * 32);
     if (!(CAUSAL && wkey0 > r0 + QB - 1)) {  // skip tiles wholly before this wave's keys
       dkdv_tile<D, NMB, decltype(masked)::value, DS>(dk, dv, Qs + cur * TILE, Ds + cur * TILE,
-                                                     rsl + cur * 2 * QB, kf, vrow, r0, key, lane,
+                                                     rsg + cur * 2 * QB, kf, vrow, r0, key, lane,
                                                      ds_pend, key_ok);
     } else if constexpr (DS) {
 #pragma unroll
@@ -661,13 +681,39 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   };
   int it = 0;
   for (; it < n_masked; ++it) step(it, std::true_type{});
-  for (; it < n_it; ++it) step(it, std::false_type{});
+  for (; it < h; ++it) step(it, std::false_type{});
   flush_ds();
+  if constexpr (G == 2) {   // group 1's dK, dV added to group 0's (then group 1 idles)
+    float* const xf = reinterpret_cast<float*>(tiles) + w * (64 * 64);
+    auto hand_over = [&](f32x16* acc) {
+      __syncthreads();
+      if (grp == 1) {
+#pragma unroll
+        for (int j = 0; j < 4 * CB; ++j)
+          *reinterpret_cast<float4*>(xf + 4 * (64 * j + lane)) =
+              make_float4(acc[j >> 2][4 * (j & 3)], acc[j >> 2][4 * (j & 3) + 1],
+                          acc[j >> 2][4 * (j & 3) + 2], acc[j >> 2][4 * (j & 3) + 3]);
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int j = 0; j < 4 * CB; ++j) {
+          const float4 x = *reinterpret_cast<const float4*>(xf + 4 * (64 * j + lane));
+          acc[j >> 2][4 * (j & 3)] += x.x;
+          acc[j >> 2][4 * (j & 3) + 1] += x.y;
+          acc[j >> 2][4 * (j & 3) + 2] += x.z;
+          acc[j >> 2][4 * (j & 3) + 3] += x.w;
+        }
+      }
+    };
+    hand_over(dk);
+    hand_over(dv);
+  }
 
   float wv[D / 4];
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
-  if (key < p.N) {
+  if (grp == 0 && key < p.N) {
     // Q~ carries log2(e)/sqrt(D): dK~ = dS^T Q~ / sqrt(D) = ln 2 * (dS^T Q~'); the
     // dO scale is undone here.  Keys below the corner get the corner's share
     // (queries below it) added by the dQ launch.
@@ -686,7 +732,7 @@ __global__ __launch_bounds__(256, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
       }
     }
   }
-  store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
+  store_dalpha<D, 4 * G>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
 }
 
 // ------------------------------------------------------------------ dQ from the dS panels
@@ -926,12 +972,27 @@ void launch_dq_mfma(const MfmaParams& p_in, hipStream_t s) {
   const int nb = dq_corner_blocks(p) + fwd_blocks(p);
   if (nb > 0) RA_LAUNCH(dq_kernel, nb);
 }
+// Dense dK/dV launches of fewer workgroups than this (two per CU of a 256-CU
+// part) split each workgroup's queries between two wave groups.
+constexpr int DKDV_SPLIT_BELOW = 512;
 void launch_dkdv_mfma(const MfmaParams& p, hipStream_t s) {
   const int nb = dkdv_blocks(p);
   if (nb <= 0) return;
   const dim3 grid((unsigned)nb), block(256);
   if (p.bmask) {
     RA_LAUNCH1(dkdv_kernel, true, false);
+  } else if (nb < DKDV_SPLIT_BELOW) {
+    const dim3 block2(512);
+    if (p.dsp) {  // D = 128 only (the library sets panels for no other D)
+      if (p.causal) hipLaunchKernelGGL((dkdv_kernel<128, true, false, true, 2>), grid, block2, 0, s, p);
+      else hipLaunchKernelGGL((dkdv_kernel<128, false, false, true, 2>), grid, block2, 0, s, p);
+    } else if (p.D == 64) {
+      if (p.causal) hipLaunchKernelGGL((dkdv_kernel<64, true, false, false, 2>), grid, block2, 0, s, p);
+      else hipLaunchKernelGGL((dkdv_kernel<64, false, false, false, 2>), grid, block2, 0, s, p);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((dkdv_kernel<128, true, false, false, 2>), grid, block2, 0, s, p);
+      else hipLaunchKernelGGL((dkdv_kernel<128, false, false, false, 2>), grid, block2, 0, s, p);
+    }
   } else if (p.dsp) {  // D = 128 only (the library sets panels for no other D)
     if (p.causal) hipLaunchKernelGGL((dkdv_kernel<128, true, false, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((dkdv_kernel<128, false, false, true>), grid, block, 0, s, p);

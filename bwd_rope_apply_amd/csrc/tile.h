@@ -408,14 +408,15 @@ __device__ __forceinline__ void accumulate_tr(f32x16* acc, const half_t* lds, co
 }
 
 // Position-weighted wedge partial of one row's gradient (already in the
-// un-rotated frame) summed over the workgroup into one [D/2] slot.
-// w[cb*8 + rq*2 + h] is pair m = 16cb + 4rq + 2g + h.
-template <int D>
+// un-rotated frame) summed over the NW waves of the workgroup into one
+// [D/2] slot (red holds NW x D/2 floats).  w[cb*8 + rq*2 + h] is pair
+// m = 16cb + 4rq + 2g + h.
+template <int D, int NW = 4>
 __device__ __forceinline__ void store_dalpha(float* w, float* red, float* slot, int g) {
-  constexpr int NW = D / 4;
+  constexpr int NP = D / 4;   // wedge partials per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
+  for (int i = 0; i < NP; ++i) {
     float x = w[i];
     x += __shfl_xor(x, 1, 64);
     x += __shfl_xor(x, 2, 64);
@@ -428,8 +429,14 @@ __device__ __forceinline__ void store_dalpha(float* w, float* red, float* slot, 
     }
   }
   __syncthreads();
-  for (int m = threadIdx.x; m < D / 2; m += 256)
-    slot[m] = (red[m] + red[D / 2 + m]) + (red[D + m] + red[3 * D / 2 + m]);
+  for (int m = threadIdx.x; m < D / 2; m += 64 * NW) {
+    float x = (red[m] + red[D / 2 + m]) + (red[D + m] + red[3 * D / 2 + m]);
+#pragma unroll
+    for (int v = 4; v < NW; v += 4)
+      x += (red[v * (D / 2) + m] + red[(v + 1) * (D / 2) + m]) +
+           (red[(v + 2) * (D / 2) + m] + red[(v + 3) * (D / 2) + m]);
+    slot[m] = x;
+  }
 }
 
 // Un-rotate one lane's gradient registers (row `row`, columns
