@@ -65,6 +65,9 @@ __host__ __device__ constexpr size_t corner_fwd_smem(int D) {
   return 3 * (size_t)corner_tile_halfs(D, CBN) * 2;
 }
 
+// Column blocks (32 columns) per pass of the corner's forward.
+constexpr int CORNER_FWD_CBP = 1;
+
 // O and LSE of query rows [128 t, 128 t + 128) below the corner (corner
 // workgroup `bid`), run as the last workgroups of the forward launch.  O is
 // built 32 columns at a time, each pass streaming the keys again (the
@@ -73,7 +76,7 @@ __host__ __device__ constexpr size_t corner_fwd_smem(int D) {
 template <int D>
 __device__ __forceinline__ void corner_fwd(const MfmaParams& p, int bid, char* smem) {
   constexpr int DT = D / 16, CB = D / 32, TILE = corner_tile_halfs(D, CBN);
-  constexpr int CBP = 1;   // column blocks (32 columns) per pass
+  constexpr int CBP = CORNER_FWD_CBP;
   half_t* Kh = reinterpret_cast<half_t*>(smem);
   half_t* Kl = Kh + TILE;
   half_t* Vs = Kl + TILE;
@@ -157,6 +160,24 @@ __device__ __forceinline__ void corner_fwd(const MfmaParams& p, int bid, char* s
         }
       }
       if (cb0 == 0 && g == 0) p.out_lse[(size_t)bh * p.N + qrow] = (m + __log2f(lt)) * LN2;
+    }
+  }
+}
+
+// The waves past the first four of a corner workgroup in a launch of 8-wave
+// workgroups: they take part in corner_fwd's barriers (two per key step,
+// per column pass) and do nothing else.
+template <int D>
+__device__ __forceinline__ void corner_fwd_idle(const MfmaParams& p, int bid) {
+  constexpr int CB = D / 32, CBP = CORNER_FWD_CBP;
+  const int q0 = (bid / (p.B * p.H)) * BM;
+  if (q0 >= p.N) return;  // whole workgroup
+  const int n_kt = min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN);
+#pragma unroll 1
+  for (int cb0 = 0; cb0 < CB; cb0 += CBP) {
+    for (int kt = 0; kt < n_kt; ++kt) {
+      __syncthreads();
+      __syncthreads();
     }
   }
 }

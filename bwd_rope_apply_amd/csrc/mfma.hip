@@ -287,13 +287,20 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dk, f32x16* dv, const half_t* 
 // the loop streams FBN-key tiles of K~ and V through double-buffered LDS,
 // the next tile's copies in flight while the current tile is computed.
 // Rows below the exact corner are skipped.
+// G: key groups.  G = 2 (launches too small to give every CU two
+// workgroups) splits each workgroup's key range between two groups of 4
+// waves on the same 128 queries, each streaming its own tiles; the second
+// group's O, m and l are merged into the first's through LDS at the end.
 constexpr int FWD_BM = 4 * 32 * FWD_NB;
 constexpr int FBN = 32 * FWD_MB;   // keys per forward step
 
-template <int D, bool CAUSAL, bool BL>
-__global__ __launch_bounds__(256, FWD_WPS) void fwd_kernel(MfmaParams p) {
+template <int D, bool CAUSAL, bool BL, int G = 1>
+__global__ __launch_bounds__(256 * G, FWD_WPS) void fwd_kernel(MfmaParams p) {
+  static_assert(G == 1 || (G == 2 && !BL && FWD_NB == 1), "key groups: dense attention, 32-row waves");
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, FBN>::ALLOC, NB = FWD_NB;
-  constexpr size_t MAIN = 4 * (size_t)TILE * sizeof(half_t);
+  constexpr size_t MAIN = G * 4 * (size_t)TILE * sizeof(half_t);
+  // G = 2 hands group 1's O (D/2 floats a lane), m and l over through the tiles
+  static_assert(G == 1 || MAIN >= 4 * 64 * (D / 2 + 2) * sizeof(float), "hand-over fits the tiles");
   // the main tiles, or a corner workgroup's tiles (the launch's last ones)
   __shared__ __attribute__((aligned(16))) char pool[MAIN > corner_fwd_smem(D) ? MAIN : corner_fwd_smem(D)];
   __shared__ short blist[BL ? MAX_BLOCKS : 1];   // block-list mode: the key blocks, ascending
@@ -301,14 +308,18 @@ __global__ __launch_bounds__(256, FWD_WPS) void fwd_kernel(MfmaParams p) {
   const int BH = p.B * p.H;
   const int ntiles = (p.N + FWD_BM - 1) / FWD_BM, t0 = p.corner / FWD_BM;
   if ((int)blockIdx.x >= BH * (ntiles - t0)) {   // the corner's split-operand rows
-    if (p.corner > 0) corner_fwd<D>(p, (int)blockIdx.x - BH * (ntiles - t0), pool);
+    if (p.corner > 0) {
+      if (G > 1 && threadIdx.x >= 256) corner_fwd_idle<D>(p, (int)blockIdx.x - BH * (ntiles - t0));
+      else corner_fwd<D>(p, (int)blockIdx.x - BH * (ntiles - t0), pool);
+    }
     return;
   }
-  half_t* Ks = reinterpret_cast<half_t*>(pool);
-  half_t* Vs = Ks + 2 * TILE;
 
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wg >> 2, w = wg & 3;   // key group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
+  half_t* Ks = reinterpret_cast<half_t*>(pool) + grp * 4 * TILE;
+  half_t* Vs = Ks + 2 * TILE;
   int bh, t;
   map_block(blockIdx.x, BH, ntiles - t0, true, bh, t);
   t += t0;
@@ -357,19 +368,30 @@ __global__ __launch_bounds__(256, FWD_WPS) void fwd_kernel(MfmaParams p) {
     n_kt = CAUSAL ? min(nk, (q0 + FWD_BM + FBN - 1) / FBN) : nk;
     split = min(n_kt, min(CAUSAL ? q0 / FBN : nk, p.N / FBN));
   }
+  // this group's steps: [0, h) for group 0, [h, n_kt) for group 1; every
+  // wave runs h steps (a group past its own count only keeps the barriers)
+  const int h = G == 1 ? n_kt : (n_kt + 1) / 2;
+  const int g_first = grp ? h : 0, n_g = grp ? n_kt - h : h;
+  const int unmasked = G == 1 ? split : min(max(split - g_first, 0), n_g);
   Walk<FBN, BL> walk;
-  walk.init(blist, 0, n_kt);
+  walk.init(blist, g_first * FBN, n_g);
 
   TileDMA<D, FBN> dma;
   dma.init(lane, w);
-  dma.load(Ks, kh, walk.cur);
-  dma.load(Vs, vh, walk.cur);
+  if (G == 1 || n_g > 0) {
+    dma.load(Ks, kh, walk.cur);
+    dma.load(Vs, vh, walk.cur);
+  }
   wait_lds_copies();
   __syncthreads();
   auto step = [&](int kt, auto masked) {
+    if (G > 1 && kt >= n_g) {
+      __syncthreads();
+      return;
+    }
     const int k0 = walk.cur;
     const int cur = (kt & 1) * TILE, nxt = TILE - cur;
-    if (kt + 1 < n_kt) {
+    if (kt + 1 < n_g) {
       dma.load(Ks + nxt, kh, walk.next);
       dma.load(Vs + nxt, vh, walk.next);
     }
@@ -383,14 +405,48 @@ __global__ __launch_bounds__(256, FWD_WPS) void fwd_kernel(MfmaParams p) {
     walk.advance(kt);
   };
   int kt = 0;
-  for (; kt < split; ++kt) step(kt, std::false_type{});
-  for (; kt < n_kt; ++kt) step(kt, std::true_type{});
+  for (; kt < unmasked; ++kt) step(kt, std::false_type{});
+  for (; kt < h; ++kt) step(kt, std::true_type{});
+
+  if constexpr (G == 2) {   // group 1's partial softmax merged into group 0's
+    float* const xf = reinterpret_cast<float*>(pool) + w * (64 * (D / 2 + 2));
+    if (grp == 1) {
+#pragma unroll
+      for (int j = 0; j < 4 * CB; ++j)
+        *reinterpret_cast<float4*>(xf + 4 * (64 * j + lane)) =
+            make_float4(o[0][j >> 2][4 * (j & 3)], o[0][j >> 2][4 * (j & 3) + 1],
+                        o[0][j >> 2][4 * (j & 3) + 2], o[0][j >> 2][4 * (j & 3) + 3]);
+      xf[64 * (D / 2) + lane] = m[0];
+      xf[64 * (D / 2 + 1) + lane] = l[0];
+    }
+    __syncthreads();
+    if (grp == 0) {
+      // both groups hold each row's reference in both of its lanes; a group
+      // that saw no key of a row has m = -inf and O = l = 0 there
+      const float m1 = xf[64 * (D / 2) + lane], l1 = xf[64 * (D / 2 + 1) + lane];
+      const float mn = fmaxf(m[0], m1);
+      const float a0 = m[0] == -INFINITY ? 0.f : exp2_fast(m[0] - mn);
+      const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - mn);
+#pragma unroll
+      for (int j = 0; j < 4 * CB; ++j) {
+        const float4 x = *reinterpret_cast<const float4*>(xf + 4 * (64 * j + lane));
+        f32x16& r = o[0][j >> 2];
+        const int e = 4 * (j & 3);
+        r[e] = r[e] * a0 + x.x * a1;
+        r[e + 1] = r[e + 1] * a0 + x.y * a1;
+        r[e + 2] = r[e + 2] * a0 + x.z * a1;
+        r[e + 3] = r[e + 3] * a0 + x.w * a1;
+      }
+      l[0] = l[0] * a0 + l1 * a1;
+      m[0] = mn;
+    }
+  }
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float lt = l[nb] + __shfl_xor(l[nb], 32, 64);
     const int row = qrow[nb];
-    if (active && row >= p.corner && row < p.N) {
+    if (grp == 0 && active && row >= p.corner && row < p.N) {
       const float inv = 1.f / lt;
       float* orow = p.o + head + (size_t)row * D;
 #pragma unroll
@@ -941,10 +997,25 @@ int dkdv_mfma_slots(const MfmaParams& p) { return dkdv_blocks(p); }
 
 // The forward launch: the row tiles past the corner, heaviest first, then
 // the corner's split-operand workgroups (beside the lightest tiles).
+// Dense forward launches of fewer main workgroups than this (two per CU of
+// a 256-CU part) split each workgroup's keys between two wave groups.
+constexpr int FWD_SPLIT_BELOW = 512;
 void launch_fwd_mfma(const MfmaParams& p, hipStream_t s) {
-  const int nb = p.B * p.H * max(0, (p.N + FWD_BM - 1) / FWD_BM - p.corner / FWD_BM) +
-                 (p.corner ? corner_blocks(p) : 0);
-  if (nb > 0) RA_LAUNCH(fwd_kernel, nb);
+  const int nmain = p.B * p.H * max(0, (p.N + FWD_BM - 1) / FWD_BM - p.corner / FWD_BM);
+  const int nb = nmain + (p.corner ? corner_blocks(p) : 0);
+  if (nb <= 0) return;
+  if (!p.bmask && nmain < FWD_SPLIT_BELOW) {
+    const dim3 grid((unsigned)nb), block(512);
+    if (p.D == 64) {
+      if (p.causal) hipLaunchKernelGGL((fwd_kernel<64, true, false, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, false, false, 2>), grid, block, 0, s, p);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((fwd_kernel<128, true, false, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<128, false, false, 2>), grid, block, 0, s, p);
+    }
+    return;
+  }
+  RA_LAUNCH(fwd_kernel, nb);
 }
 // The corner workgroups (latency-bound chains of a few to a few tens of
 // steps) come last in the dQ launch's grid: the grid issues the heaviest dQ
