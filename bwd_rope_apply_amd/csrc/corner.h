@@ -360,6 +360,25 @@ __device__ __forceinline__ void corner_kv(const MfmaParams& p, int bid, int slot
   store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
 }
 
+// The waves past the first four of a corner workgroup in a dQ launch of
+// 8-wave workgroups: they take part in the corner body's barriers and do
+// nothing else.  corner_dq has two per 32-key step, corner_kv two per
+// 32-row query step, and each one more in its d alpha reduction.
+template <int D>
+__device__ __forceinline__ void corner_bwd_idle(const MfmaParams& p, int bid) {
+  const int n = corner_blocks(p), BH = p.B * p.H;
+  int steps;
+  if (bid < n) {   // corner_dq's n_kt
+    const int q0 = (bid / BH) * BM;
+    steps = q0 < p.N ? min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN) : 0;
+  } else {         // corner_kv's steps r0 = k0, k0 + CBN, ... below nlo
+    const int k0 = ((bid - (bid < 2 * n ? n : 2 * n)) / BH) * BM;
+    const int nlo = min(p.N, p.corner);
+    steps = k0 < nlo ? (nlo - k0 + CBN - 1) / CBN : 0;
+  }
+  for (int i = 0; i < 2 * steps + 1; ++i) __syncthreads();
+}
+
 // The corner workgroups of a dQ launch: [0, n) take dQ rows, [n, 2 n) the
 // dV shares and [2 n, 3 n) the dK shares (n = corner_blocks); slots follow
 // the workgroup index.

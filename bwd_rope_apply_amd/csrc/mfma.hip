@@ -821,27 +821,35 @@ constexpr int DQP_STAGES = 3;
 
 // NJ: 32-row query blocks per wave, 2 (a whole panel per workgroup) or 1 (half
 // a panel, for launches too small to fill the GPU otherwise).
-template <int D, bool CAUSAL, int NJ>
-__global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
+// G: key groups.  G = 2 (half panels, launches still too small to give
+// every CU two workgroups) splits each workgroup's key tiles between two
+// groups of 4 waves on the same query rows, each with its own ring; the
+// second group's dQ~ is added to the first's through LDS at the end.
+template <int D, bool CAUSAL, int NJ, int G = 1>
+__global__ __launch_bounds__(256 * G, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
+  static_assert(G == 1 || (G == 2 && NJ == 1), "key groups: half panels");
   constexpr int CB = D / 32, TK = TileDMA<D, DQP_KB>::ALLOC, TS = DQP_TS * NJ / 2;
   constexpr int NS = DQP_STAGES;
   static_assert(TS * 2 == NJ * 8 * 1024, "2 NJ 1 KiB copies per wave per panel tile");
-  constexpr size_t MAIN = (size_t)NS * (TK + TS) * sizeof(half_t);
-  // the ring, or a corner workgroup's tiles (the launch's first ones)
+  constexpr size_t RING = (size_t)NS * (TK + TS) * sizeof(half_t), MAIN = G * RING;
+  static_assert(G == 1 || MAIN >= 4 * 64 * NJ * (D / 2) * sizeof(float), "hand-over fits the rings");
+  // the rings, or a corner workgroup's tiles (the launch's last ones)
   __shared__ __attribute__((aligned(16))) char pool[MAIN > corner_bwd_smem(D) ? MAIN : corner_bwd_smem(D)];
-  __shared__ float red[4 * (D / 2)];
+  __shared__ float red[4 * G * (D / 2)];
   const int ncorner = p.corner ? 3 * corner_blocks(p) : 0;
   const int bx = (int)blockIdx.x;
   if (bx >= p.corner_at && bx < p.corner_at + ncorner) {
-    corner_bwd<D>(p, bx - p.corner_at, pool);
+    if (G > 1 && threadIdx.x >= 256) corner_bwd_idle<D>(p, bx - p.corner_at);
+    else corner_bwd<D>(p, bx - p.corner_at, pool);
     return;
   }
   const int mb = bx < p.corner_at ? bx : bx - ncorner;   // this workgroup's panel (half)
-  half_t* Ks = reinterpret_cast<half_t*>(pool);
-  half_t* Ss = Ks + NS * TK;
 
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wg >> 2, w = wg & 3;   // key group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
+  half_t* Ks = reinterpret_cast<half_t*>(pool + grp * RING);
+  half_t* Ss = Ks + NS * TK;
   const int BH = p.B * p.H;
   const int np = n_panels(p.N), t0 = p.corner / PANEL;
   int bh, u;
@@ -856,7 +864,12 @@ __global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
   // keys of this panel below N, in whole tiles (the panel rows are a
   // multiple of the tile; a ragged last tile holds zeros past N)
   const int nkeys = min(panel_rows(t, p.N, CAUSAL), (p.N + DQP_KB - 1) / DQP_KB * DQP_KB);
-  const int n_kt = nkeys / DQP_KB;
+  const int n_kt_all = nkeys / DQP_KB;
+  // this group's tiles: [0, h) for group 0, [h, n_kt_all) for group 1, as
+  // steps 0 .. n_kt - 1 from kt0; every wave runs h steps (a group past its
+  // own count only keeps the barriers)
+  const int h = G == 1 ? n_kt_all : (n_kt_all + 1) / 2;
+  const int kt0 = grp ? h : 0, n_kt = grp ? n_kt_all - h : h;
 
   f32x16 acc[NJ][CB];
 #pragma unroll
@@ -885,10 +898,10 @@ __global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
   };
   auto load = [&](int kt) {
     const int b = kt % NS;
-    dmk.load(Ks + b * TK, kh, kt * DQP_KB);
+    dmk.load(Ks + b * TK, kh, (kt0 + kt) * DQP_KB);
     // the panel tile (this half's query blocks): 1 KiB blocks wave + 4 i,
     // lane l at byte 16 l
-    const uint32_t tb = (uint32_t)kt * (uint32_t)(2 * DQP_TS) + 8192u * (uint32_t)hb;
+    const uint32_t tb = (uint32_t)(kt0 + kt) * (uint32_t)(2 * DQP_TS) + 8192u * (uint32_t)hb;
 #pragma unroll
     for (int i = 0; i < PC; ++i)
       lds_copy16_nt(panel, tb + 1024u * (wave + 4 * i) + 16u * lane, Ss + b * TS + (wave + 4 * i) * 512);
@@ -899,8 +912,12 @@ __global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
   }
   wait_landed(n_kt >= NS - 1);   // tile 0
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * DQP_KB;
+  for (int kt = 0; kt < h; ++kt) {
+    if (G > 1 && kt >= n_kt) {   // this group is done (its copies all landed)
+      __syncthreads();
+      continue;
+    }
+    const int k0 = (kt0 + kt) * DQP_KB;
     // ring slot offsets as opaque scalars: the fragment addresses are then one
     // add each, not offsets the compiler derives from kt per read
     const int slot = __builtin_amdgcn_readfirstlane(kt % NS);
@@ -933,6 +950,29 @@ __global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
     wait_landed(kt + NS - 1 < n_kt);   // tile kt + 1
     __syncthreads();
   }
+  if constexpr (G == 2) {   // group 1's dQ~ added to group 0's (then group 1 idles)
+    float* const xf = reinterpret_cast<float*>(pool) + w * (64 * (D / 2));
+    if (grp == 1) {
+#pragma unroll
+      for (int j = 0; j < 4 * CB; ++j)
+        *reinterpret_cast<float4*>(xf + 4 * (64 * j + lane)) =
+            make_float4(acc[0][j >> 2][4 * (j & 3)], acc[0][j >> 2][4 * (j & 3) + 1],
+                        acc[0][j >> 2][4 * (j & 3) + 2], acc[0][j >> 2][4 * (j & 3) + 3]);
+    }
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < 4 * CB; ++j) {
+        const float4 x = *reinterpret_cast<const float4*>(xf + 4 * (64 * j + lane));
+        f32x16& r = acc[0][j >> 2];
+        const int e = 4 * (j & 3);
+        r[e] += x.x;
+        r[e + 1] += x.y;
+        r[e + 2] += x.z;
+        r[e + 3] += x.w;
+      }
+    }
+  }
 
   float wv[D / 4], wj[D / 4];
 #pragma unroll
@@ -940,7 +980,7 @@ __global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int qrow = wrow0 + 32 * j + l32;
-    if (active && qrow >= p.corner && qrow < p.N) {
+    if (grp == 0 && active && qrow >= p.corner && qrow < p.N) {
       finish_rows<D>(acc[j], p.scale * dscale_inv(p.dsc, bh), nullptr, p.cs + (size_t)qrow * (D / 2), p.q,
                      head + (size_t)qrow * D, p.bf16, p.dq + head + (size_t)qrow * D, (float)qrow,
                      wj, g);
@@ -948,7 +988,7 @@ __global__ __launch_bounds__(256, DQ_WPS) void dq_panel_kernel(MfmaParams p) {
       for (int i = 0; i < D / 4; ++i) wv[i] += wj[i];
     }
   }
-  store_dalpha<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
+  store_dalpha<D, 4 * G>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
 }
 
 int fwd_blocks(const MfmaParams& p) {  // dQ workgroups: 128-row tiles past the corner
@@ -967,6 +1007,9 @@ int dq_panel_blocks(const MfmaParams& p) {  // panels (halves) past the corner
   const int np = n_panels(p.N) - p.corner / PANEL;
   return np > 0 ? p.B * p.H * np * (dq_panel_half(p) ? 2 : 1) : 0;
 }
+// Half-panel launches of fewer workgroups than this also split each
+// workgroup's key tiles between two wave groups.
+constexpr int DQP_SPLIT_BELOW = 512;
 
 }  // namespace
 
@@ -1030,7 +1073,11 @@ void launch_dq_mfma(const MfmaParams& p_in, hipStream_t s) {
     const int nb = dq_corner_blocks(p) + dq_panel_blocks(p);
     const dim3 grid((unsigned)nb), block(256);
     if (nb <= 0) return;
-    if (dq_panel_half(p)) {
+    if (dq_panel_half(p) && dq_panel_blocks(p) < DQP_SPLIT_BELOW) {
+      const dim3 block2(512);
+      if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true, 1, 2>), grid, block2, 0, s, p);
+      else hipLaunchKernelGGL((dq_panel_kernel<128, false, 1, 2>), grid, block2, 0, s, p);
+    } else if (dq_panel_half(p)) {
       if (p.causal) hipLaunchKernelGGL((dq_panel_kernel<128, true, 1>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((dq_panel_kernel<128, false, 1>), grid, block, 0, s, p);
     } else {

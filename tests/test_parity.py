@@ -270,6 +270,14 @@ def test_bf16_panels_whole_panel_mode_ragged(causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
+def test_bf16_half_panels_one_group_ragged(causal):
+    """Half panels per workgroup (fewer than 512 whole panels) with one wave
+    group each (at least 512 halves: 2 x 64 heads x 3 panels x 2); smaller
+    launches split each half panel's keys between two wave groups."""
+    _check(W.make_inputs(W.get("layer_2k", B=2, H=64, N=600, seed=4600)), causal=causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
 def test_panels_and_recomputation_agree(causal):
     """The two dQ passes on the same inputs: dK and dV come from the same
     dK/dV kernel arithmetic (bit-identical); dQ and dalpha sum the same dS
