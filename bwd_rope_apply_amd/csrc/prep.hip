@@ -9,25 +9,41 @@
 
 namespace ra {
 
+// Each thread takes one band m over a run of TABLE_RUN consecutive
+// positions: theta_hat_m and the run's first angle are evaluated directly,
+// and each later position turns the previous (cos, sin) by theta_hat_m
+// (angle addition, in double: the error grows by a few units of 2^-53 a
+// step, far below the float rounding).  Consecutive threads take
+// consecutive bands, so each position's row is stored contiguously.
+constexpr int TABLE_RUN = 8;
+
 __global__ void table_kernel(TableParams p) {
   const int half = p.D / 2;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)p.N * half) return;
+  const int runs = (p.N + TABLE_RUN - 1) / TABLE_RUN;
+  if (idx >= (long)runs * half) return;
   const int m = (int)(idx % half);
-  const int pos = (int)(idx / half);
+  const int pos0 = (int)(idx / half) * TABLE_RUN;
   const double a = p.alpha ? (double)p.alpha[m] : 0.0;
   // unrotated bands (partial RoPE) have rate 0: angle 0, and a zero alpha
   // gradient through the theta_hat factor
   const double th = m < p.rot ? exp(a) * pow(p.base, -2.0 * (double)m / (double)p.D) : 0.0;
-  if (pos == 0) p.theta_hat[m] = th;
+  if (pos0 == 0) p.theta_hat[m] = th;
   if (idx == 0 && p.flags) *p.flags = 0u;
-  double s, c;
-  sincos((double)(pos + p.pos0) * th, &s, &c);
-  p.cs[idx] = make_float2((float)c, (float)s);
+  double s, c, sd, cd;
+  sincos((double)(pos0 + p.pos0) * th, &s, &c);
+  sincos(th, &sd, &cd);
+  const int n = min(TABLE_RUN, p.N - pos0);
+  for (int i = 0; i < n; ++i) {
+    p.cs[(size_t)(pos0 + i) * half + m] = make_float2((float)c, (float)s);
+    const double cn = c * cd - s * sd;
+    s = s * cd + c * sd;
+    c = cn;
+  }
 }
 
 void launch_table(const TableParams& p, hipStream_t s) {
-  const long n = (long)p.N * (p.D / 2);
+  const long n = (long)((p.N + TABLE_RUN - 1) / TABLE_RUN) * (p.D / 2);
   hipLaunchKernelGGL(table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
 }
 
