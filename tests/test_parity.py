@@ -278,6 +278,15 @@ def test_bf16_half_panels_one_group_ragged(causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
+def test_bf16_d64_one_group_launches(causal):
+    """D = 64 with launches of at least 512 workgroups (2 x 64 heads x 600:
+    512 forward and 640 dK/dV workgroups), so the forward and dK/dV keep one
+    wave group per workgroup; the small D = 64 cases split them in two."""
+    wl = dataclasses.replace(W.get("vlong_32k", B=2, H=64, N=600, seed=6400), causal=causal)
+    _check(W.make_inputs(wl), causal=causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
 def test_panels_and_recomputation_agree(causal):
     """The two dQ passes on the same inputs: dK and dV come from the same
     dK/dV kernel arithmetic (bit-identical); dQ and dalpha sum the same dS
