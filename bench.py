@@ -10,12 +10,16 @@ Throughput is algorithmic: 6 B H N^2 D flops per step (the two forward
 products and the four backward products over the causal half), the standard
 count for causal attention training; recomputation of scores in the backward
 is not counted (the FlashAttention convention, which adds it, 7 B H N^2 D, is
-reported beside it).  Durations come from HIP events recorded on the stream
-the library launches on (torch's current stream), between the staged entry
-points: the timed step is the forward in one call and the backward in four
-(the dK/dV kernel alone in one of them, for the roofline), so the timed work
-is exactly the full forward + backward.  A few untimed steps afterwards run
-every kernel in its own call for the per-kernel breakdown (stages_ms_serial).
+reported beside it).  The step time is the host's clock around the timed
+steps, bracketed by device synchronisations.  The timed step is the forward
+in one call and the backward in four (the dK/dV kernel alone in one of
+them), so the timed work is exactly the full forward + backward; HIP events
+on the stream the library launches on (torch's current stream) bracket the
+dK/dV call in every timed step, for the roofline, and nothing else (each
+event record costs the GPU a few microseconds).  Untimed steps afterwards
+repeat the timed step with an event before every call (calls_ms, events_ms),
+and run every kernel in its own call for the per-kernel breakdown
+(stages_ms_serial).
 One workspace serves both passes: the backward reuses the forward's rotated
 fp16 planes and frequency table (saved activations) and prepares only dO
 and D.
@@ -397,7 +401,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(fwd_calls, bwd_calls, events=None):
+    def step(fwd_calls, bwd_calls, events=None, dom_events=None):
+        """One fwd + bwd step.  events: one before each call and one at the
+        end (the breakdown pass); dom_events: one before and one after the
+        dominant call only (the timed steps: each event record costs the GPU
+        a few microseconds, so the timed steps carry just these two)."""
         i = 0
         for name, bit in fwd_calls:
             if events is not None:
@@ -408,8 +416,12 @@ def main():
         for name, bit in bwd_calls:
             if events is not None:
                 events[i].record()
+            if dom_events is not None and name == DOMINANT[0]:
+                dom_events[0].record()
             _lib.bwd(q, k, v, o, do, lse, wl.base, alpha, wl.causal, workspace=ws_b,
                      out=(dq, dk, dv, da), stages=bit, opts=opts)
+            if dom_events is not None and name == DOMINANT[0]:
+                dom_events[1].record()
             i += 1
         if events is not None:
             events[i].record()
@@ -418,19 +430,27 @@ def main():
     for _ in range(args.warmup):
         step(FWD_CALLS, BWD_CALLS)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-          for _ in range(args.steps)]
+    ev_dom = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(FWD_CALLS, BWD_CALLS, ev[s])
+        step(FWD_CALLS, BWD_CALLS, dom_events=ev_dom[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if not (torch.isfinite(o).all() and torch.isfinite(dq).all() and torch.isfinite(dk).all()
             and torch.isfinite(dv).all() and torch.isfinite(da).all()):
         print("bench.py: non-finite outputs", file=sys.stderr)
         sys.exit(1)
+    # the dominant call's average over the timed steps (the roofline's duration)
+    dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_dom]))
 
+    # breakdown pass after the timed steps: the same steps with an event
+    # before every call (per-call times, fwd / bwd medians)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(FWD_CALLS, BWD_CALLS, ev[s])
+    torch.cuda.synchronize()
     call_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
                for i, n in enumerate(calls)}
     nf = len(FWD_CALLS)
@@ -463,11 +483,11 @@ def main():
 
     dom, kernel, dom_units = DOMINANT
     if wl.dtype == "bf16":
-        achieved = dom_units * unit / (call_ms[dom] * 1e-3) / 1e12
+        achieved = dom_units * unit / (dom_ms * 1e-3) / 1e12
         traffic = measured_traffic(args.traffic, dom, wl.name) if args.retrieved < 0 else None
         roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                    "traffic": traffic, "avg_ms": round(call_ms[dom], 4)}
+                    "traffic": traffic, "avg_ms": round(dom_ms, 4)}
         if clocks:
             # the same peak at the clock the kernel actually ran at
             ghz = clocks["sclk_ghz_under_" + kernel]
