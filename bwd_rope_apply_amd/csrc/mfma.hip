@@ -52,13 +52,15 @@ constexpr int DKDV_WPS = 2;
 // MASK hides keys after klim[nb] (causal diagonal, ragged tail).
 constexpr float LAZY_LIMIT = 32768.f;   // 2^15: every P <= this fits fp16
 
+// seed: the accumulators' starting values per row block (null: zero)
 template <int D, int NB, int MB>
 __device__ __forceinline__ void fwd_scores(f32x16 (*s)[MB], const half_t* Ks,
-                                           const half8 (*qf)[D / 16], int l32, int g) {
+                                           const half8 (*qf)[D / 16], int l32, int g,
+                                           const f32x16* seed = nullptr) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb][mb] = f32x16{};
+    for (int nb = 0; nb < NB; ++nb) s[nb][mb] = seed ? seed[nb] : f32x16{};
     const half_t* row = Ks + sig(32 * mb + perm(l32)) * (D + 8) + 8 * g;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
@@ -69,17 +71,22 @@ __device__ __forceinline__ void fwd_scores(f32x16 (*s)[MB], const half_t* Ks,
   }
 }
 
+// negm: at D = 64 (SEEDED), -m of each row in all 16 registers of a block,
+// the score products' starting value, so that they come out as S - m; at
+// D = 128 the registers are short (three waves per SIMD), and the step
+// subtracts m from the scores instead.
 template <int D, int NB, bool MASK, int MB = 2>
-__device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l,
+__device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l, f32x16* negm,
                                          const half_t* Ks, const half_t* Vs,
                                          const half8 (*qf)[D / 16], int k0, const int* klim,
                                          int lane) {
+  constexpr bool SEEDED = D == 64;
   const int l32 = lane & 31, g = lane >> 5;
   // the scheduler's LDS-read / MFMA interleaving strategy: more fragment
   // reads stay ahead of the products
   __builtin_amdgcn_iglp_opt(0);
   f32x16 s[NB][MB];
-  fwd_scores<D, NB, MB>(s, Ks, qf, l32, g);
+  fwd_scores<D, NB, MB>(s, Ks, qf, l32, g, SEEDED ? negm : nullptr);
   // scores minus the reference, masked keys at -inf
   auto relative = [&](int nb, float ref) {
 #pragma unroll
@@ -124,13 +131,16 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
   bool exact = false;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    relative(nb, m[nb]);
+    if (!SEEDED || MASK) relative(nb, SEEDED ? 0.f : m[nb]);   // seeded: the mask only
     exps(nb);
     ls[nb] = weights(nb);
     // NaN (m = -inf) and +inf (a weight past fp16) fail the test too
     exact |= m[nb] == -INFINITY || !(ls[nb] <= LAZY_LIMIT);
   }
   if (__any(exact)) {  // rare: the scores again, and the reference to the row maximum
+    // seeded: the fragments are read again rather than kept live through the
+    // exps, which leaves the registers the seed blocks take
+    if constexpr (SEEDED) asm volatile("" ::: "memory");
     fwd_scores<D, NB, MB>(s, Ks, qf, l32, g);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -149,6 +159,10 @@ __device__ __forceinline__ void fwd_tile(f32x16 (*o)[D / 32], float* m, float* l
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb) o[nb][cb] *= alpha;
       m[nb] = mn;
+      if constexpr (SEEDED) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[nb][r] = -mn;
+      }
       const float ref = mn == -INFINITY ? 0.f : mn;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -333,6 +347,7 @@ __global__ __launch_bounds__(256 * G, FWD_WPS) void fwd_kernel(MfmaParams p) {
   half8 qf[NB][DT];
   int qrow[NB], klim[NB];
   f32x16 o[NB][CB];
+  f32x16 negm[NB];   // -m (D = 64 seeds the score products with it)
   float m[NB], l[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -343,6 +358,8 @@ __global__ __launch_bounds__(256 * G, FWD_WPS) void fwd_kernel(MfmaParams p) {
     for (int cb = 0; cb < CB; ++cb) o[nb][cb] = f32x16{};
     m[nb] = -INFINITY;
     l[nb] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[nb][r] = INFINITY;
   }
   const int wlast = wrow0 + 32 * NB - 1;
   // steps before `split` need no mask for any wave (the workgroup's diagonal
@@ -398,7 +415,7 @@ __global__ __launch_bounds__(256 * G, FWD_WPS) void fwd_kernel(MfmaParams p) {
     walk.prefetch(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the next tile's copies ahead of the compute
     if (active && !(CAUSAL && k0 > wlast))  // skip tiles wholly above this wave's rows
-      fwd_tile<D, NB, decltype(masked)::value, FWD_MB>(o, m, l, Ks + cur, Vs + cur, qf, k0, klim,
+      fwd_tile<D, NB, decltype(masked)::value, FWD_MB>(o, m, l, negm, Ks + cur, Vs + cur, qf, k0, klim,
                                                        lane);
     wait_lds_copies();
     __syncthreads();
