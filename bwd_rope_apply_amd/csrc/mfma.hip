@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256 * G, DKDV_WPS) void dkdv_kernel(MfmaParams p) {
   constexpr int QB = DKDV_BN, NMB = QB / 32;
   constexpr int DT = D / 16, CB = D / 32, TILE = TileDMA<D, QB>::ALLOC;
   // each group's double-buffered Q~ and dO tiles; G = 2 also reuses them
-  // for the dK, dV hand-over (4 waves x 64 lanes x 64 floats)
+  // for the dK, dV hand-over (4 waves x 64 lanes x D/2 floats)
   static_assert(G == 1 || 2 * G * 2 * TILE * 2 >= 4 * 64 * (D / 2) * 4, "hand-over fits the tiles");
   __shared__ __attribute__((aligned(16))) half_t tiles[G * 2 * 2 * TILE];
   __shared__ __attribute__((aligned(16))) half_t Vst[BM * (D + 8)];
