@@ -51,8 +51,8 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // at 4 x 32 x 4096 with groups of 4: dK/dV -2.5%, dQ from panels -5.6%
 // against all 16 heads interleaved; groups of 2 made the forward and the
 // dQ product slower at 1 x 32 x 8192 and left dK/dV unchanged).
-__device__ __forceinline__ void map_block(int idx, int BH, int ntiles, bool heavy_high, int& bh,
-                                          int& t, int group = 4) {
+__host__ __device__ __forceinline__ void map_block(int idx, int BH, int ntiles, bool heavy_high,
+                                                   int& bh, int& t, int group = 4) {
   int k;
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;
