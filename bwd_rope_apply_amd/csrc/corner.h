@@ -68,6 +68,20 @@ __host__ __device__ constexpr size_t corner_fwd_smem(int D) {
 // Column blocks (32 columns) per pass of the corner's forward.
 constexpr int CORNER_FWD_CBP = 1;
 
+// Step counts of the corner bodies.  Every step of a body holds two
+// barriers, so the idle waves of an 8-wave workgroup (corner_fwd_idle,
+// corner_bwd_idle) take their counts from these same functions.
+// Key steps of the forward and dQ bodies for the 128-row query block at q0:
+__device__ __forceinline__ int corner_q_steps(const MfmaParams& p, int q0) {
+  return q0 < p.N ? min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN) : 0;
+}
+// Query steps of the dK, dV share bodies for the key block at k0 (the query
+// rows below the corner, from k0 on):
+__device__ __forceinline__ int corner_kv_steps(const MfmaParams& p, int k0) {
+  const int nlo = min(p.N, p.corner);
+  return k0 < nlo ? (nlo - k0 + CBN - 1) / CBN : 0;
+}
+
 // O and LSE of query rows [128 t, 128 t + 128) below the corner (corner
 // workgroup `bid`), run as the last workgroups of the forward launch.  O is
 // built 32 columns at a time, each pass streaming the keys again (the
@@ -92,7 +106,7 @@ __device__ __forceinline__ void corner_fwd(const MfmaParams& p, int bid, char* s
   load_frag_rows<D>(qf, p.qh + head, qrow, p.N, g);
   load_frag_rows<D>(ql, p.qlo + lhead, qrow, nlo, g);
   const int klim = min(qrow, p.N - 1);
-  const int n_kt = min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN);
+  const int n_kt = corner_q_steps(p, q0);
   const bool row_ok = qrow < p.N && qrow < p.corner;
   float* orow = p.o + head + (size_t)qrow * D;
 #pragma unroll 1
@@ -172,7 +186,7 @@ __device__ __forceinline__ void corner_fwd_idle(const MfmaParams& p, int bid) {
   constexpr int CB = D / 32, CBP = CORNER_FWD_CBP;
   const int q0 = (bid / (p.B * p.H)) * BM;
   if (q0 >= p.N) return;  // whole workgroup
-  const int n_kt = min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN);
+  const int n_kt = corner_q_steps(p, q0);
 #pragma unroll 1
   for (int cb0 = 0; cb0 < CB; cb0 += CBP) {
     for (int kt = 0; kt < n_kt; ++kt) {
@@ -218,7 +232,7 @@ __device__ __forceinline__ void corner_dq(const MfmaParams& p, int bid, int slot
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
   const int klim = min(qrow, p.N - 1);
-  const int n_kt = q0 < p.N ? min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN) : 0;
+  const int n_kt = corner_q_steps(p, q0);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * CBN;
     __syncthreads();
@@ -287,7 +301,9 @@ __device__ __forceinline__ void corner_kv(const MfmaParams& p, int bid, int slot
   f32x16 acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
-  for (int r0 = k0; r0 < nlo; r0 += CBN) {
+  const int n_st = corner_kv_steps(p, k0);
+  for (int st = 0; st < n_st; ++st) {
+    const int r0 = k0 + st * CBN;
     __syncthreads();
     stage3<D, CBN>(Qh, p.qh + head, Ql, p.qlo + lhead, Ds, p.doh + head, r0, p.N, nlo);
     if (threadIdx.x < CBN) {
@@ -367,15 +383,8 @@ __device__ __forceinline__ void corner_kv(const MfmaParams& p, int bid, int slot
 template <int D>
 __device__ __forceinline__ void corner_bwd_idle(const MfmaParams& p, int bid) {
   const int n = corner_blocks(p), BH = p.B * p.H;
-  int steps;
-  if (bid < n) {   // corner_dq's n_kt
-    const int q0 = (bid / BH) * BM;
-    steps = q0 < p.N ? min((p.N + CBN - 1) / CBN, (q0 + BM + CBN - 1) / CBN) : 0;
-  } else {         // corner_kv's steps r0 = k0, k0 + CBN, ... below nlo
-    const int k0 = ((bid - (bid < 2 * n ? n : 2 * n)) / BH) * BM;
-    const int nlo = min(p.N, p.corner);
-    steps = k0 < nlo ? (nlo - k0 + CBN - 1) / CBN : 0;
-  }
+  const int steps = bid < n ? corner_q_steps(p, (bid / BH) * BM)
+                            : corner_kv_steps(p, ((bid - (bid < 2 * n ? n : 2 * n)) / BH) * BM);
   for (int i = 0; i < 2 * steps + 1; ++i) __syncthreads();
 }
 
