@@ -39,12 +39,13 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 __device__ __forceinline__ int pi32(int m) { return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1); }
 
 // Rows [r0, r0 + FT) of one head into an LDS tile [FT][LD] as fp32,
-// rotated when cs != null; rows outside [0, N) are zero.  128 threads.
+// rotated when cs != null; rows outside [0, N) are zero.  128 threads, tid
+// in [0, 128).
 template <int D, int LD>
 __device__ __forceinline__ void stage_f32(float* dst, const void* src, size_t head_off, int r0,
-                                          int N, int bf16, const float2* cs) {
+                                          int N, int bf16, const float2* cs, int tid) {
   constexpr int CH = D / 4;
-  for (int t = threadIdx.x; t < FT * CH; t += 128) {
+  for (int t = tid; t < FT * CH; t += 128) {
     const int r = t / CH, c = (t % CH) * 4;
     const int row = r0 + r;
     float x[4] = {0.f, 0.f, 0.f, 0.f};
@@ -105,35 +106,82 @@ __device__ __forceinline__ void accumulate_t32(f32x16* acc, const float* tile, c
   }
 }
 
-// The wedge partials of a two-wave workgroup (finish_rows' layout) summed
-// into one [D/2] slot.
+// The wedge partials of the first two waves of a workgroup (finish_rows'
+// layout) summed into one [D/2] slot; every thread of the workgroup calls
+// it (one barrier), waves past the first two hold no partials.
 template <int D>
 __device__ __forceinline__ void store_dalpha2(float* w, float* red, float* slot, int g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave < 2) {
 #pragma unroll
-  for (int i = 0; i < D / 4; ++i) {
-    float x = w[i];
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
-    x += __shfl_xor(x, 16, 64);
-    if ((lane & 31) == 0) {
-      const int cb = i >> 3, rq = (i >> 1) & 3, h = i & 1;
-      red[wave * (D / 2) + 16 * cb + 4 * rq + 2 * g + h] = x;
+    for (int i = 0; i < D / 4; ++i) {
+      float x = w[i];
+      x += __shfl_xor(x, 1, 64);
+      x += __shfl_xor(x, 2, 64);
+      x += __shfl_xor(x, 4, 64);
+      x += __shfl_xor(x, 8, 64);
+      x += __shfl_xor(x, 16, 64);
+      if ((lane & 31) == 0) {
+        const int cb = i >> 3, rq = (i >> 1) & 3, h = i & 1;
+        red[wave * (D / 2) + 16 * cb + 4 * rq + 2 * g + h] = x;
+      }
     }
   }
   __syncthreads();
   for (int m = threadIdx.x; m < D / 2; m += 128) slot[m] = red[m] + red[D / 2 + m];
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(128) void f32_fwd_kernel(SimtParams p) {
-  constexpr int LD = D + 4, CB = D / 32;
-  __shared__ __attribute__((aligned(16))) float ks[FT * LD];
-  __shared__ __attribute__((aligned(16))) float vs[FT * LD];
+// G: groups of 128 threads per workgroup.  Launches too small to fill the
+// GPU (tiny problems are bound by each workgroup's chain of steps) split the
+// streamed range (keys in the forward and dQ, queries in dK/dV) between G
+// groups on the same rows; each group stages its own tiles, every thread
+// runs the same number of steps (a group past its own range only keeps the
+// barriers), and groups 1 .. G-1 hand their partial results to group 0
+// through the staging tiles, which adds them in that order.
+
+// This group's steps of a range of n: [first, first + count), count <= h.
+struct GroupSteps {
+  int h, first, count;
+  __device__ GroupSteps(int n, int G, int grp) {
+    h = (n + G - 1) / G;
+    first = grp * h;
+    count = max(0, min(n - first, h));
+  }
+};
+
+// Hands over NV floats a lane (x[0 .. NV)) from each group past the first
+// to group 0 through buf ((G - 1) x 128 x NV floats); merge(x, j) runs in
+// group 0 for j = 1 .. G-1 in order.  Every thread calls it (two barriers).
+template <int G, int NV, typename Put, typename Merge>
+__device__ __forceinline__ void hand_over(float* buf, int grp, int tid, Put put, Merge merge) {
+  __syncthreads();   // every group is done with the staging tiles
+  if (grp > 0) {
+    float x[NV];
+    put(x);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) buf[((grp - 1) * NV + v) * 128 + tid] = x[v];
+  }
+  __syncthreads();
+  if (grp == 0) {
+    for (int j = 1; j < G; ++j) {
+      float x[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) x[v] = buf[((j - 1) * NV + v) * 128 + tid];
+      merge(x, j);
+    }
+  }
+}
+
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(128 * G) void f32_fwd_kernel(SimtParams p) {
+  constexpr int LD = D + 4, CB = D / 32, TSZ = FT * LD;
+  static_assert(G == 1 || 2 * G * TSZ >= (G - 1) * 128 * (16 * CB + 2), "hand-over fits the tiles");
+  __shared__ __attribute__((aligned(16))) float pool[G * 2 * TSZ];
   const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int grp = threadIdx.x >> 7, tid = threadIdx.x & 127;
+  const int lane = threadIdx.x & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  float* ks = pool + grp * 2 * TSZ;
+  float* vs = ks + TSZ;
   const int r0 = blockIdx.x * FW, q = r0 + 32 * w + l32;   // this lane's query
   const size_t head = (size_t)bh * p.N * D;
   float qf[D / 2];
@@ -143,11 +191,17 @@ __global__ __launch_bounds__(128) void f32_fwd_kernel(SimtParams p) {
   for (int cb = 0; cb < CB; ++cb) o[cb] = f32x16{};
   float m = -INFINITY, l = 0.f;
   const int kend = CAUSAL ? min(p.N, r0 + FW) : p.N;
-  for (int k0 = 0; k0 < kend; k0 += FT) {
+  const GroupSteps st((kend + FT - 1) / FT, G, grp);
+  for (int i = 0; i < st.h; ++i) {
+    const int k0 = (st.first + i) * FT;
+    const bool mine = i < st.count;
     __syncthreads();
-    stage_f32<D, LD>(ks, p.k, head, k0, p.N, p.bf16, p.cs);
-    stage_f32<D, LD>(vs, p.v, head, k0, p.N, p.bf16, nullptr);
+    if (mine) {
+      stage_f32<D, LD>(ks, p.k, head, k0, p.N, p.bf16, p.cs, tid);
+      stage_f32<D, LD>(vs, p.v, head, k0, p.N, p.bf16, nullptr, tid);
+    }
     __syncthreads();
+    if (!mine) continue;
     f32x16 s = score32<D, LD>(ks, qf, l32, g);   // register r: key k0 + 2r + g
     float mx = -INFINITY;
 #pragma unroll
@@ -173,8 +227,34 @@ __global__ __launch_bounds__(128) void f32_fwd_kernel(SimtParams p) {
     m = mn;
     accumulate_t32<D, LD>(o, vs, s, l32, g);   // O^T += V^T P^T
   }
+  if constexpr (G > 1) {
+    // partial softmax states (each row's max is the same in both of its
+    // lanes; a group that saw no key of a row has m = -inf, O = l = 0)
+    hand_over<G, 16 * CB + 2>(pool, grp, tid,
+        [&](float* x) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[16 * cb + r] = o[cb][r];
+          }
+          x[16 * CB] = m;
+          x[16 * CB + 1] = l;
+        },
+        [&](const float* x, int) {
+          const float mj = x[16 * CB], mn = fmaxf(m, mj);
+          const float a0 = m == -INFINITY ? 0.f : expf(m - mn);
+          const float aj = mj == -INFINITY ? 0.f : expf(mj - mn);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[cb][r] = o[cb][r] * a0 + x[16 * cb + r] * aj;
+          }
+          l = l * a0 + x[16 * CB + 1] * aj;
+          m = mn;
+        });
+  }
   l += __shfl_xor(l, 32, 64);
-  if (q < p.N) {
+  if (grp == 0 && q < p.N) {
     const float inv = 1.f / l;
     float* orow = p.out_o + head + (size_t)q * D;
 #pragma unroll
@@ -191,14 +271,17 @@ __global__ __launch_bounds__(128) void f32_fwd_kernel(SimtParams p) {
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(128) void f32_dq_kernel(SimtParams p) {
-  constexpr int LD = D + 4, CB = D / 32;
-  __shared__ __attribute__((aligned(16))) float ks[FT * LD];
-  __shared__ __attribute__((aligned(16))) float vs[FT * LD];
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(128 * G) void f32_dq_kernel(SimtParams p) {
+  constexpr int LD = D + 4, CB = D / 32, TSZ = FT * LD;
+  static_assert(G == 1 || 2 * G * TSZ >= (G - 1) * 128 * (16 * CB), "hand-over fits the tiles");
+  __shared__ __attribute__((aligned(16))) float pool[G * 2 * TSZ];
   __shared__ float red[2 * (D / 2)];
   const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int grp = threadIdx.x >> 7, tid = threadIdx.x & 127;
+  const int lane = threadIdx.x & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  float* ks = pool + grp * 2 * TSZ;
+  float* vs = ks + TSZ;
   const int r0 = blockIdx.x * FW, q = r0 + 32 * w + l32;
   const size_t head = (size_t)bh * p.N * D;
   float qf[D / 2], df[D / 2];
@@ -211,11 +294,17 @@ __global__ __launch_bounds__(128) void f32_dq_kernel(SimtParams p) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
   const int kend = CAUSAL ? min(p.N, r0 + FW) : p.N;
-  for (int k0 = 0; k0 < kend; k0 += FT) {
+  const GroupSteps st((kend + FT - 1) / FT, G, grp);
+  for (int i = 0; i < st.h; ++i) {
+    const int k0 = (st.first + i) * FT;
+    const bool mine = i < st.count;
     __syncthreads();
-    stage_f32<D, LD>(ks, p.k, head, k0, p.N, p.bf16, p.cs);
-    stage_f32<D, LD>(vs, p.v, head, k0, p.N, p.bf16, nullptr);
+    if (mine) {
+      stage_f32<D, LD>(ks, p.k, head, k0, p.N, p.bf16, p.cs, tid);
+      stage_f32<D, LD>(vs, p.v, head, k0, p.N, p.bf16, nullptr, tid);
+    }
     __syncthreads();
+    if (!mine) continue;
     f32x16 s = score32<D, LD>(ks, qf, l32, g);    // S^T: register r, key k0 + 2r + g
     const f32x16 dp = score32<D, LD>(vs, df, l32, g);   // (dO V^T)^T
 #pragma unroll
@@ -227,49 +316,80 @@ __global__ __launch_bounds__(128) void f32_dq_kernel(SimtParams p) {
     }
     accumulate_t32<D, LD>(acc, ks, s, l32, g);   // dQ~^T += K~^T dS^T
   }
+  if constexpr (G > 1) {
+    hand_over<G, 16 * CB>(pool, grp, tid,
+        [&](float* x) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[16 * cb + r] = acc[cb][r];
+          }
+        },
+        [&](const float* x, int) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[cb][r] += x[16 * cb + r];
+          }
+        });
+  }
   float wv[D / 4];
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
-  if (q_ok)
+  if (grp == 0 && q_ok)
     finish_rows<D>(acc, p.scale, nullptr, p.cs + (size_t)q * (D / 2), p.q, head + (size_t)q * D,
                    p.bf16, p.dq + head + (size_t)q * D, (float)q, wv, g);
   const int slot = p.slot0 + bh * gridDim.x + blockIdx.x;
   store_dalpha2<D>(wv, red, p.dalpha_part + (size_t)slot * (D / 2), g);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(128) void f32_dkdv_kernel(SimtParams p) {
-  constexpr int LD = D + 4, CB = D / 32;
-  __shared__ __attribute__((aligned(16))) float qs[FT * LD];
-  __shared__ __attribute__((aligned(16))) float dos[FT * LD];
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(128 * G) void f32_dkdv_kernel(SimtParams p) {
+  constexpr int LD = D + 4, CB = D / 32, TSZ = FT * LD;
+  // the hand-over goes dK then dV, 16 CB floats a lane each
+  static_assert(G == 1 || 2 * G * TSZ >= (G - 1) * 128 * (16 * CB), "hand-over fits the tiles");
+  __shared__ __attribute__((aligned(16))) float pool[G * 2 * TSZ];
   __shared__ __attribute__((aligned(16))) float vst[FW * LD];   // this workgroup's V rows
-  __shared__ float lses[FT], drs[FT];
+  __shared__ float lsg[G][2][FT];   // each group's row scalars: LSE, D
   __shared__ float red[2 * (D / 2)];
   const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int grp = threadIdx.x >> 7, tid = threadIdx.x & 127;
+  const int lane = threadIdx.x & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  float* qs = pool + grp * 2 * TSZ;
+  float* dos = qs + TSZ;
+  float* lses = lsg[grp][0];
+  float* drs = lsg[grp][1];
   const int k0 = blockIdx.x * FW, key = k0 + 32 * w + l32;   // this lane's key
   const size_t head = (size_t)bh * p.N * D;
   const bool key_ok = key < p.N;
   float kf[D / 2];
   row_frags<D>(kf, p.k, head, key, p.N, p.bf16, p.cs, g);
-  stage_f32<D, LD>(vst, p.v, head, k0, p.N, p.bf16, nullptr);
-  stage_f32<D, LD>(vst + FT * LD, p.v, head, k0 + FT, p.N, p.bf16, nullptr);
+  if (grp == 0) {   // published by the first step's barrier
+    stage_f32<D, LD>(vst, p.v, head, k0, p.N, p.bf16, nullptr, tid);
+    stage_f32<D, LD>(vst + FT * LD, p.v, head, k0 + FT, p.N, p.bf16, nullptr, tid);
+  }
   const float* vrow = vst + (32 * w + l32) * LD + g;   // B elements of dP: V[key][2 kk + g]
   f32x16 dk[CB], dv[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) { dk[cb] = f32x16{}; dv[cb] = f32x16{}; }
   const int qstart = CAUSAL ? k0 : 0;
-  for (int r0 = qstart; r0 < p.N; r0 += FT) {
+  const GroupSteps st(qstart < p.N ? (p.N - qstart + FT - 1) / FT : 0, G, grp);
+  for (int i = 0; i < st.h; ++i) {
+    const int r0 = qstart + (st.first + i) * FT;
+    const bool mine = i < st.count;
     __syncthreads();
-    stage_f32<D, LD>(qs, p.q, head, r0, p.N, p.bf16, p.cs);
-    stage_f32<D, LD>(dos, p.dO, head, r0, p.N, p.bf16, nullptr);
-    if (threadIdx.x < FT) {
-      const int row = r0 + threadIdx.x;
-      const bool ok = row < p.N;
-      lses[threadIdx.x] = ok ? p.lse[(size_t)bh * p.N + row] : 0.f;
-      drs[threadIdx.x] = ok ? p.drow[(size_t)bh * p.N + row] : 0.f;
+    if (mine) {
+      stage_f32<D, LD>(qs, p.q, head, r0, p.N, p.bf16, p.cs, tid);
+      stage_f32<D, LD>(dos, p.dO, head, r0, p.N, p.bf16, nullptr, tid);
+      if (tid < FT) {
+        const int row = r0 + tid;
+        const bool ok = row < p.N;
+        lses[tid] = ok ? p.lse[(size_t)bh * p.N + row] : 0.f;
+        drs[tid] = ok ? p.drow[(size_t)bh * p.N + row] : 0.f;
+      }
     }
     __syncthreads();
+    if (!mine) continue;
     f32x16 s = score32<D, LD>(qs, kf, l32, g);   // S: register r, query r0 + 2r + g
     f32x16 dp = {};
     {
@@ -279,19 +399,41 @@ __global__ __launch_bounds__(128) void f32_dkdv_kernel(SimtParams p) {
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = 2 * r + g, row = r0 + i;
+      const int i2 = 2 * r + g, row = r0 + i2;
       const bool ok = key_ok && row < p.N && (!CAUSAL || row >= key);
-      const float pr = ok ? expf(s[r] * p.scale - lses[i]) : 0.f;
+      const float pr = ok ? expf(s[r] * p.scale - lses[i2]) : 0.f;
       s[r] = pr;
-      dp[r] = pr * (dp[r] - drs[i]);   // dS
+      dp[r] = pr * (dp[r] - drs[i2]);   // dS
     }
     accumulate_t32<D, LD>(dv, dos, s, l32, g);   // dV^T += dO^T P
     accumulate_t32<D, LD>(dk, qs, dp, l32, g);   // dK~^T += Q~^T dS
   }
+  if constexpr (G > 1) {
+    auto put = [](const f32x16* a) {
+      return [a](float* x) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[16 * cb + r] = a[cb][r];
+        }
+      };
+    };
+    auto add = [](f32x16* a) {
+      return [a](const float* x, int) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[cb][r] += x[16 * cb + r];
+        }
+      };
+    };
+    hand_over<G, 16 * CB>(pool, grp, tid, put(dk), add(dk));
+    hand_over<G, 16 * CB>(pool, grp, tid, put(dv), add(dv));
+  }
   float wv[D / 4];
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) wv[i] = 0.f;
-  if (key_ok) {
+  if (grp == 0 && key_ok) {
     finish_rows<D>(dk, p.scale, nullptr, p.cs + (size_t)key * (D / 2), p.k, head + (size_t)key * D,
                    p.bf16, p.dk + head + (size_t)key * D, (float)key, wv, g);
     float* dvrow = p.dv + head + (size_t)key * D;
@@ -313,15 +455,32 @@ dim3 f32_grid(const SimtParams& p) {
   return dim3((unsigned)((p.N + FW - 1) / FW), (unsigned)p.BH);
 }
 
-#define RA_F32_LAUNCH(KERNEL)                                                                  \
-  do {                                                                                         \
-    if (p.D == 64) {                                                                           \
-      if (p.causal) hipLaunchKernelGGL((KERNEL<64, true>), f32_grid(p), dim3(128), 0, s, p);   \
-      else hipLaunchKernelGGL((KERNEL<64, false>), f32_grid(p), dim3(128), 0, s, p);           \
-    } else {                                                                                   \
-      if (p.causal) hipLaunchKernelGGL((KERNEL<128, true>), f32_grid(p), dim3(128), 0, s, p);  \
-      else hipLaunchKernelGGL((KERNEL<128, false>), f32_grid(p), dim3(128), 0, s, p);          \
-    }                                                                                          \
+// Groups per workgroup: 4 (D = 64 only: the tiles of four groups fit the
+// LDS beside dK/dV's V rows) for launches of at most 64 workgroups, 2 for at
+// most 256, else 1.
+int f32_groups(const SimtParams& p) {
+  const long nwg = (long)((p.N + FW - 1) / FW) * p.BH;
+  if (nwg <= 64 && p.D == 64) return 4;
+  return nwg <= 256 ? 2 : 1;
+}
+
+#define RA_F32_LAUNCH_DG(KERNEL, DD, G)                                                       \
+  do {                                                                                        \
+    if (p.causal) hipLaunchKernelGGL((KERNEL<DD, true, G>), grid, dim3(128 * (G)), 0, s, p);  \
+    else hipLaunchKernelGGL((KERNEL<DD, false, G>), grid, dim3(128 * (G)), 0, s, p);          \
+  } while (0)
+#define RA_F32_LAUNCH(KERNEL)                                              \
+  do {                                                                     \
+    const dim3 grid = f32_grid(p);                                         \
+    const int groups = f32_groups(p);                                      \
+    if (p.D == 64) {                                                       \
+      if (groups == 4) RA_F32_LAUNCH_DG(KERNEL, 64, 4);                    \
+      else if (groups == 2) RA_F32_LAUNCH_DG(KERNEL, 64, 2);               \
+      else RA_F32_LAUNCH_DG(KERNEL, 64, 1);                                \
+    } else {                                                               \
+      if (groups == 2) RA_F32_LAUNCH_DG(KERNEL, 128, 2);                   \
+      else RA_F32_LAUNCH_DG(KERNEL, 128, 1);                               \
+    }                                                                      \
   } while (0)
 
 }  // namespace

@@ -81,6 +81,19 @@ def test_fp32_lengths(N, D):
     _check(W.make_inputs(wl))
 
 
+@pytest.mark.parametrize("H,D,causal", [(40, 64, True), (300, 64, True), (300, 64, False),
+                                         (300, 128, True), (40, 128, False)])
+def test_fp32_group_counts(H, D, causal):
+    """The fp32 kernels split each workgroup's streamed range between 4
+    groups of waves for launches of at most 64 workgroups (D = 64), 2 for
+    at most 256, and keep one group above that: 40 heads x 2 workgroups take
+    two groups, 300 heads one; the small cases elsewhere take four (D = 64)
+    or two (D = 128).  N = 150 gives a ragged tail."""
+    wl = W.Workload("fp32_groups", 1, H, 150, D, "fp32", 1e4, causal, ("normal", 1.0, 1.0),
+                    ("normal", 1.0, 1.0), ("normal", 1.0, 1.0), ("normal", 0.3, 1.0), seed=700 + H + D)
+    _check(W.make_inputs(wl), causal=causal)
+
+
 @pytest.mark.parametrize("name", ["layer_2k", "train_4k", "long_8k", "vlong_32k"])
 def test_bf16_workloads_reduced_length(name):
     """Each bf16 workload's distributions at N = 700 (corner + several
