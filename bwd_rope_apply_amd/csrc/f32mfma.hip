@@ -19,9 +19,11 @@
 // 8(m/8) + 2(m%4) + (m/4)%2, so register r of lane (n, g) holds the score
 // of row 2r + g: exactly the B operand element of k step r of the next
 // product, with no data movement between lanes.  Tiles are fp32 in LDS,
-// [32][D + 4], staged (and rotated) from the inputs; each workgroup is two
-// waves of 32 rows (or keys), the same 64-row blocks as the vector path, so
-// the d alpha partial slots are the same.
+// [32][D + 4], staged (and rotated) from the inputs; each workgroup owns 64
+// rows (or keys) as two waves of 32, the same 64-row blocks as the vector
+// path, so the d alpha partial slots are the same.  Small launches give a
+// workgroup 2 or 4 such pairs of waves, each over part of the streamed
+// range (see GroupSteps below).
 #include "tile.h"
 
 namespace ra {
